@@ -1,0 +1,9 @@
+"""MI355X-native chunked forward of Kimi Delta Attention (KDA).
+
+The compute path is the HIP library ``libkda.so`` (C ABI in ``include/kda.h``);
+``kda`` is its ctypes binding.  Build with ``python -m gated_delta_rule_chunked_amd.build``.
+"""
+from .kda import (  # noqa: F401
+    KDA_CHUNK, KdaError, KdaFwdArgs, alloc_workspace, kda_debug_unpack, kda_fwd, kda_fwd_inter,
+    kda_fwd_intra, kda_fwd_raw, kda_fwd_workspace_bytes, kda_strerror, load_library, make_args,
+)

@@ -1,0 +1,163 @@
+// kda_api.cpp -- the C ABI declared in include/kda.h: host-side validation,
+// workspace sizing and kernel launches on the caller's stream.  No allocation,
+// no synchronisation, no state kept between calls.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/kda.h"
+#include "kda_device.hpp"
+#include "kda_internal.hpp"
+
+namespace {
+
+thread_local char g_hip_msg[256] = "no HIP error recorded";
+
+bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+int64_t rec_bytes(int K) { return K == 128 ? kda::Rec<128>::BYTES : kda::Rec<64>::BYTES; }
+
+// Shape checks shared by every entry point.  Fills the layout on success.
+int check_shapes(const kda_fwd_args* a, kda::WsLayout* L) {
+  if (!a) return KDA_ERR_INVALID_ARG;
+  if (a->K != 64 && a->K != 128) return KDA_ERR_UNSUPPORTED;
+  if (a->V <= 0 || a->V % kda::BV != 0) return KDA_ERR_UNSUPPORTED;
+  if (a->B < 1 || a->T < 0 || a->HQK < 1 || a->HV < 1 || a->N < 1) return KDA_ERR_INVALID_ARG;
+  if (a->HV % a->HQK != 0) return KDA_ERR_INVALID_ARG;
+  if (a->cu_seqlens) {
+    if (a->B != 1) return KDA_ERR_INVALID_ARG;
+  } else if (a->N != a->B) {
+    return KDA_ERR_INVALID_ARG;
+  }
+  // every element index must fit in int64 and every grid in int32
+  const int64_t rows = (int64_t)a->B * a->T;
+  if (rows > ((int64_t)1 << 40)) return KDA_ERR_INVALID_ARG;
+  const int64_t nt = ((int64_t)a->T + kda::BT - 1) / kda::BT;
+  const int64_t max_chunks = a->cu_seqlens ? nt + a->N : (int64_t)a->B * nt;
+  if (max_chunks * a->HV >= ((int64_t)1 << 31) - 8) return KDA_ERR_INVALID_ARG;
+  if ((int64_t)a->N * a->HV * (a->V / kda::BV) >= ((int64_t)1 << 31) - 8) return KDA_ERR_INVALID_ARG;
+  if (a->N >= (1 << 30)) return KDA_ERR_INVALID_ARG;
+  L->rec_bytes = rec_bytes(a->K);
+  L->max_chunks = max_chunks;
+  L->table_bytes = a->cu_seqlens ? (((int64_t)a->N + 2) * 4 + 255) / 256 * 256 : 0;
+  L->total_bytes = L->table_bytes + max_chunks * a->HV * L->rec_bytes;
+  return KDA_OK;
+}
+
+enum Need { NEED_INTRA = 1, NEED_INTER = 2 };
+
+int check_call(const kda_fwd_args* a, int need, kda::Params* p) {
+  kda::WsLayout L;
+  int st = check_shapes(a, &L);
+  if (st != KDA_OK) return st;
+  const bool any_tokens = (int64_t)a->B * a->T > 0;
+  if (need & NEED_INTRA) {
+    if (any_tokens && (!a->q || !a->k || !a->g || !a->beta)) return KDA_ERR_INVALID_ARG;
+    if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->g, 16) || !aligned(a->beta, 2))
+      return KDA_ERR_INVALID_ARG;
+  }
+  if (need & NEED_INTER) {
+    if (any_tokens && (!a->v || !a->o)) return KDA_ERR_INVALID_ARG;
+    if (!aligned(a->v, 16) || !aligned(a->o, 2) || !aligned(a->h0, 16) || !aligned(a->ht, 16))
+      return KDA_ERR_INVALID_ARG;
+  }
+  if (!aligned(a->cu_seqlens, 8)) return KDA_ERR_INVALID_ARG;
+  if (L.total_bytes > 0) {
+    if (!a->workspace || !aligned(a->workspace, 256)) return KDA_ERR_WORKSPACE;
+    if (a->workspace_bytes < (size_t)L.total_bytes) return KDA_ERR_WORKSPACE;
+  }
+  if (!(a->scale == a->scale)) return KDA_ERR_INVALID_ARG;  // NaN scale
+  p->q = (const uint16_t*)a->q;
+  p->k = (const uint16_t*)a->k;
+  p->v = (const uint16_t*)a->v;
+  p->g = (const uint16_t*)a->g;
+  p->beta = (const uint16_t*)a->beta;
+  p->h0 = a->h0;
+  p->cu = a->cu_seqlens;
+  p->o = (uint16_t*)a->o;
+  p->ht = a->ht;
+  p->table = a->cu_seqlens ? (int32_t*)a->workspace : nullptr;
+  p->recs = (uint8_t*)a->workspace + L.table_bytes;
+  p->scale = a->scale;
+  p->B = a->B; p->T = a->T; p->HQK = a->HQK; p->HV = a->HV; p->K = a->K; p->V = a->V; p->N = a->N;
+  p->NT = (int)(((int64_t)a->T + kda::BT - 1) / kda::BT);
+  p->max_chunks = L.max_chunks;
+  return KDA_OK;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return KDA_OK;
+  strncpy(g_hip_msg, hipGetErrorString(e), sizeof(g_hip_msg) - 1);
+  g_hip_msg[sizeof(g_hip_msg) - 1] = 0;
+  return KDA_ERR_HIP;
+}
+
+int run_intra(const kda::Params& p, hipStream_t s) {
+  if (p.cu) {
+    int st = hip_status(kda::launch_chunk_table(p, s));
+    if (st != KDA_OK) return st;
+  }
+  return hip_status(kda::launch_intra(p, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_fwd_workspace_bytes(const kda_fwd_args* a, size_t* bytes) {
+  if (!bytes) return KDA_ERR_INVALID_ARG;
+  kda::WsLayout L;
+  int st = check_shapes(a, &L);
+  if (st != KDA_OK) return st;
+  *bytes = (size_t)L.total_bytes;
+  return KDA_OK;
+}
+
+int kda_fwd_intra(const kda_fwd_args* a) {
+  kda::Params p;
+  int st = check_call(a, NEED_INTRA, &p);
+  if (st != KDA_OK) return st;
+  return run_intra(p, (hipStream_t)a->stream);
+}
+
+int kda_fwd_inter(const kda_fwd_args* a) {
+  kda::Params p;
+  int st = check_call(a, NEED_INTER, &p);
+  if (st != KDA_OK) return st;
+  return hip_status(kda::launch_inter(p, (hipStream_t)a->stream));
+}
+
+int kda_fwd(const kda_fwd_args* a) {
+  kda::Params p;
+  int st = check_call(a, NEED_INTRA | NEED_INTER, &p);
+  if (st != KDA_OK) return st;
+  st = run_intra(p, (hipStream_t)a->stream);
+  if (st != KDA_OK) return st;
+  return hip_status(kda::launch_inter(p, (hipStream_t)a->stream));
+}
+
+int kda_debug_unpack(const kda_fwd_args* a, void* qg, void* w, void* kg, void* aqk, void* tmb,
+                     float* alpha) {
+  kda::Params p;
+  int st = check_call(a, 0, &p);
+  if (st != KDA_OK) return st;
+  const void* outs[] = {qg, w, kg, aqk, tmb, alpha};
+  for (const void* ptr : outs)
+    if (!aligned(ptr, 16)) return KDA_ERR_INVALID_ARG;
+  return hip_status(kda::launch_unpack(p, (uint16_t*)qg, (uint16_t*)w, (uint16_t*)kg, (uint16_t*)aqk,
+                                       (uint16_t*)tmb, alpha, (hipStream_t)a->stream));
+}
+
+const char* kda_strerror(int status) {
+  switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size or head counts)";
+    case KDA_ERR_UNSUPPORTED: return "unsupported shape (K must be 64 or 128, V a positive multiple of 16)";
+    case KDA_ERR_WORKSPACE: return "workspace missing, not 256-byte aligned, or smaller than kda_fwd_workspace_bytes";
+    case KDA_ERR_HIP: return g_hip_msg;
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

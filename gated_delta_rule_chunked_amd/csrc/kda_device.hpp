@@ -1,0 +1,132 @@
+// kda_device.hpp -- device helpers and the workspace record layout shared by the
+// intra-chunk and inter-chunk kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int BT = 64;        // chunk length (tokens)
+constexpr int BV = 16;        // value columns per inter-chunk workgroup
+constexpr int NTHREADS = 256; // 4 waves per workgroup, both kernels
+constexpr float LOG2E = 1.4426950408889634f;
+
+typedef short bf16x8 __attribute__((ext_vector_type(8)));
+typedef short bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2n __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------------ MFMA
+// v_mfma_f32_16x16x32_bf16, lane l = 16*g + r (g = l/16, r = l%16):
+//   A (16 x 32): lane holds A[r][8g .. 8g+7]
+//   B (32 x 16): lane holds B[8g .. 8g+7][r]
+//   C (16 x 16): lane holds C[4g .. 4g+3][r]
+__device__ __forceinline__ f32x4 mfma16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// v_mfma_f32_16x16x4_f32 (fp32 operands): A lane holds A[r][g], B lane holds
+// B[g][r], C as above.
+__device__ __forceinline__ f32x4 mfma16x4f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf2f(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+__device__ __forceinline__ float bflo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bfhi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+// Two floats -> packed bf16 pair (round to nearest even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2n));
+}
+__device__ __forceinline__ uint16_t f2bf(float x) { return (uint16_t)(pack2(x, 0.f) & 0xffffu); }
+
+// 8 bf16 (one uint4) <-> 8 floats
+__device__ __forceinline__ void unpack8(const uint4& u, float* f) {
+  f[0] = bflo(u.x); f[1] = bfhi(u.x); f[2] = bflo(u.y); f[3] = bfhi(u.y);
+  f[4] = bflo(u.z); f[5] = bfhi(u.z); f[6] = bflo(u.w); f[7] = bfhi(u.w);
+}
+__device__ __forceinline__ uint4 pack8(const float* f) {
+  return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
+}
+__device__ __forceinline__ bf16x8 as_frag(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+// ------------------------------------------------------------ DPP scans
+// Inclusive prefix sum over the 16 lanes of each DPP row (lanes 16g .. 16g+15),
+// in lane order.  row_shr:n moves lane i-n to lane i inside a row; lanes with
+// no source receive 0 (bound_ctrl).
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+  int v = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xf, 0xf, true);
+  return __builtin_bit_cast(float, v);
+}
+__device__ __forceinline__ float row_inclusive_scan(float x) {
+  x += row_shr<1>(x);
+  x += row_shr<2>(x);
+  x += row_shr<4>(x);
+  x += row_shr<8>(x);
+  return x;
+}
+
+// ----------------------------------------------------- block -> XCD remap
+// Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD
+// b % 8).  Remapping makes consecutive logical ids share an XCD and its L2, so
+// the value tiles of one head (inter kernel) and the two value heads of one q/k
+// head (intra kernel) meet in the same L2.  Correctness never depends on it.
+// `grid` must be a multiple of 8.
+__device__ __forceinline__ int xcd_remap(int b, int grid) {
+  return (b & 7) * (grid >> 3) + (b >> 3);
+}
+
+// ---------------------------------------------------- workspace records
+// One record per (chunk, value head), written by the intra kernel in the exact
+// register-fragment order the inter kernel consumes, so every inter-kernel
+// operand load is one contiguous 1 KiB wave load (16 B per lane).
+//
+//   QG  : A operand of  O = qg h     [64 x K] bf16, scale folded in
+//   WN  : A operand of  v' = u + (-w) h   [64 x K] bf16 (negated w)
+//   KGT : A operand of  DH = kg^T v'  [K x 64] bf16
+//   AQK : A operand of  O += Aqk v'   [64 x 64] bf16 lower triangle
+//   TMB : A operand of  u = (Tm diag beta) v   [64 x 64] bf16 lower triangle
+//   ALPHA: exp2(G) per key dimension, fp32 [K]
+//
+// [64 x K] fragments (QG, WN): frag (mb, s), mb = row block 0..3, s = 32-column
+//   step 0..K/32-1; lane l holds row 16mb + l%16, columns 32s + 8(l/16) .. +7.
+//   byte offset ((mb * K/32 + s) * 64 + l) * 16.
+// KGT fragments: frag (md, s), md = 16-row block of the key dimension 0..K/16-1,
+//   s = 0,1 (token halves); lane l holds d = 16md + l%16, tokens 32s + 8(l/16) ..
+//   +7.  byte offset ((md * 2 + s) * 64 + l) * 16.
+// AQK / TMB: lower-triangular 64 x 64, the two all-zero fragments (rows 0..31,
+//   columns 32..63) are not stored: frag index (mb, s) -> {0,1,2,3,4,5} for
+//   (0,0),(1,0),(2,0),(2,1),(3,0),(3,1); lane layout as QG.
+template <int K>
+struct Rec {
+  static constexpr int S = K / 32;                 // 32-wide K steps
+  static constexpr int QG = 0;
+  static constexpr int WN = QG + BT * K * 2;
+  static constexpr int KGT = WN + BT * K * 2;
+  static constexpr int AQK = KGT + BT * K * 2;
+  static constexpr int TMB = AQK + 6 * 1024;
+  static constexpr int ALPHA = TMB + 6 * 1024;
+  static constexpr int BYTES = ALPHA + K * 4;      // 61952 (K=128), 37120 (K=64)
+  static_assert(BYTES % 256 == 0, "records stay 256-byte aligned");
+};
+__device__ __host__ __forceinline__ constexpr int tri_frag(int mb, int s) {
+  return mb < 2 ? mb : 2 * mb - 2 + s;   // (0,0)0 (1,0)1 (2,0)2 (2,1)3 (3,0)4 (3,1)5
+}
+__device__ __host__ __forceinline__ constexpr int tri_steps(int mb) { return mb < 2 ? 1 : 2; }
+
+// Layout of the workspace: [table area | records], table area = varlen chunk
+// table (int32 chunk_base[N+1]) + an int32 error flag, padded to 256 bytes.
+struct WsLayout {
+  int64_t table_bytes;
+  int64_t rec_bytes;
+  int64_t max_chunks;   // capacity in chunks per value head
+  int64_t total_bytes;
+};
+
+}  // namespace kda

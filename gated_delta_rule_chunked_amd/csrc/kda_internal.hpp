@@ -1,0 +1,35 @@
+// kda_internal.hpp -- kernel parameters and host-side launch entry points shared
+// by the C ABI (kda_api.cpp) and the kernel files.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct Params {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* g;
+  const uint16_t* beta;
+  const float* h0;
+  const int64_t* cu;     // varlen cu_seqlens or nullptr
+  uint16_t* o;
+  float* ht;
+  int32_t* table;        // varlen: chunk_base[N+1], then error flag at [N+1]
+  uint8_t* recs;         // workspace records
+  float scale;
+  int B, T, HQK, HV, K, V, N;
+  int NT;                // fixed length: chunks per sequence
+  int64_t max_chunks;    // workspace capacity in chunks (per value head)
+};
+
+// Host launchers (return the hipError_t of the launch).
+hipError_t launch_chunk_table(const Params& p, hipStream_t s);
+hipError_t launch_intra(const Params& p, hipStream_t s);
+hipError_t launch_inter(const Params& p, hipStream_t s);
+hipError_t launch_unpack(const Params& p, uint16_t* qg, uint16_t* w, uint16_t* kg,
+                         uint16_t* aqk, uint16_t* tmb, float* alpha, hipStream_t s);
+
+}  // namespace kda

@@ -1,0 +1,176 @@
+"""Python binding of the C ABI in ``include/kda.h`` (ctypes).
+
+Argument marshalling only: every step of the forward runs in the HIP kernels of
+``libkda.so``.  PyTorch supplies device memory (outputs, workspace) and the
+current stream.  There is no CPU fallback: if the library is missing or no GPU
+is present, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import c_float, c_int, c_int32, c_size_t, c_void_p
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_OK = 0
+KDA_ERR_INVALID_ARG = -1
+KDA_ERR_UNSUPPORTED = -2
+KDA_ERR_WORKSPACE = -3
+KDA_ERR_HIP = -4
+KDA_CHUNK = 64
+
+EXPORTED = ("kda_fwd_workspace_bytes", "kda_fwd", "kda_fwd_intra", "kda_fwd_inter",
+            "kda_debug_unpack", "kda_strerror")
+
+
+class KdaFwdArgs(ctypes.Structure):
+    """Mirror of ``kda_fwd_args`` (field order and types as in the header)."""
+    _fields_ = [
+        ("q", c_void_p), ("k", c_void_p), ("v", c_void_p), ("g", c_void_p), ("beta", c_void_p),
+        ("scale", c_float), ("h0", c_void_p), ("cu_seqlens", c_void_p),
+        ("B", c_int32), ("T", c_int32), ("HQK", c_int32), ("HV", c_int32),
+        ("K", c_int32), ("V", c_int32), ("N", c_int32),
+        ("o", c_void_p), ("ht", c_void_p),
+        ("workspace", c_void_p), ("workspace_bytes", c_size_t),
+        ("stream", c_void_p),
+    ]
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: status {status}: {kda_strerror(status)}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load ``libkda.so`` once.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m gated_delta_rule_chunked_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(KdaFwdArgs)
+    lib.kda_fwd_workspace_bytes.argtypes = [P, ctypes.POINTER(c_size_t)]
+    for name in ("kda_fwd", "kda_fwd_intra", "kda_fwd_inter"):
+        getattr(lib, name).argtypes = [P]
+        getattr(lib, name).restype = c_int
+    lib.kda_fwd_workspace_bytes.restype = c_int
+    lib.kda_debug_unpack.argtypes = [P] + [c_void_p] * 6
+    lib.kda_debug_unpack.restype = c_int
+    lib.kda_strerror.argtypes = [c_int]
+    lib.kda_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def kda_strerror(status: int) -> str:
+    return load_library().kda_strerror(status).decode()
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def make_args(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, o=None, ht=None,
+              workspace=None, stream=None) -> KdaFwdArgs:
+    """Fill ``kda_fwd_args`` from torch tensors (shapes as in the header).
+
+    q, k: [B, T, HQK, K] bf16; v: [B, T, HV, V] bf16; g: [B, T, HV, K] bf16;
+    beta: [B, T, HV] bf16; h0: [N, HV, K, V] fp32 or None; cu_seqlens: int64 [N+1]
+    on the device or None.  Only pointers and sizes are read here.
+    """
+    import torch
+    B, T, HQK, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16), ("v", v, torch.bfloat16),
+                        ("g", g, torch.bfloat16), ("beta", beta, torch.bfloat16),
+                        ("h0", h0, torch.float32), ("cu_seqlens", cu_seqlens, torch.int64),
+                        ("o", o, torch.bfloat16), ("ht", ht, torch.float32)):
+        if t is not None:
+            if t.dtype != dt:
+                raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    a = KdaFwdArgs()
+    a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
+    a.scale = float(K ** -0.5 if scale is None else scale)
+    a.h0, a.cu_seqlens = _ptr(h0), _ptr(cu_seqlens)
+    a.B, a.T, a.HQK, a.HV, a.K, a.V, a.N = B, T, HQK, HV, K, V, N
+    a.o, a.ht = _ptr(o), _ptr(ht)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    a.stream = stream
+    return a
+
+
+def kda_fwd_workspace_bytes(args: KdaFwdArgs) -> int:
+    n = c_size_t(0)
+    st = load_library().kda_fwd_workspace_bytes(ctypes.byref(args), ctypes.byref(n))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_fwd_workspace_bytes")
+    return n.value
+
+
+def _call(name: str, args: KdaFwdArgs) -> None:
+    st = getattr(load_library(), name)(ctypes.byref(args))
+    if st != KDA_OK:
+        raise KdaError(st, name)
+
+
+def kda_fwd_raw(args: KdaFwdArgs) -> None:
+    _call("kda_fwd", args)
+
+
+def kda_fwd_intra(args: KdaFwdArgs) -> None:
+    _call("kda_fwd_intra", args)
+
+
+def kda_fwd_inter(args: KdaFwdArgs) -> None:
+    _call("kda_fwd_inter", args)
+
+
+def alloc_workspace(args: KdaFwdArgs, device):
+    import torch
+    n = kda_fwd_workspace_bytes(args)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def kda_fwd(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, output_final_state=True,
+            o=None, workspace=None):
+    """Chunked KDA forward on the current stream; returns (o, ht or None).
+
+    Allocates o, ht and the workspace with torch unless given.
+    """
+    import torch
+    if not q.is_cuda:
+        raise RuntimeError("kda_fwd runs on the GPU only (tensors must be on a HIP device)")
+    load_library()
+    B, T, _, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if o is None:
+        o = torch.empty((B, T, HV, V), dtype=torch.bfloat16, device=q.device)
+    ht = torch.empty((N, HV, K, V), dtype=torch.float32, device=q.device) if output_final_state else None
+    args = make_args(q, k, v, g, beta, scale, h0, cu_seqlens, o, ht)
+    if workspace is None:
+        workspace = alloc_workspace(args, q.device)
+    args.workspace = workspace.data_ptr()
+    args.workspace_bytes = workspace.numel() * workspace.element_size()
+    kda_fwd_raw(args)
+    return o, ht
+
+
+def kda_debug_unpack(args: KdaFwdArgs, qg=None, w=None, kg=None, aqk=None, tmb=None, alpha=None):
+    st = load_library().kda_debug_unpack(ctypes.byref(args), _ptr(qg), _ptr(w), _ptr(kg), _ptr(aqk),
+                                         _ptr(tmb), _ptr(alpha))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_debug_unpack")

@@ -1,0 +1,130 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) chunked forward of Kimi Delta Attention.
+ *
+ * The method (one value head, one sequence):
+ *     S_t = (I - beta_t k_t k_t^T) diag(exp g_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t
+ * computed in chunks of 64 tokens: an intra-chunk stage (per-dimension cumulative
+ * gate, gated Aqk, the UT/WY inverse, w, u, qg, kg) and a serial inter-chunk state
+ * scan that keeps h [K, V] in fp32:
+ *     v' = u - w h,   o = scale * qg h + Aqk v',   h <- diag(exp2 G) h + kg^T v'.
+ * Sources: "kernel-fun 0.2.0.dev1 -- kernel_fun/kda/_kernels/fwd_state.py",
+ * module docstring (the chunk operands and the state scan) and host wrapper
+ * (the call contract: bf16 operands, fp32 h0/ht [B, HV, K, V]); "KDA源码剖析之
+ * FlashKDA（下）", the recurrence kernel's phases 3-6 (u = (v - k_decayed S) beta,
+ * U = INV u, out = q_decayed S + Mqk U, S <- g_total S + k_restored^T U) and the
+ * sequence-information section (varlen via cu_seqlens, one state per sequence).
+ *
+ * Conventions for every entry point below
+ *   - Tensor pointers are DEVICE pointers to contiguous row-major memory; the
+ *     caller owns every buffer.  The library never allocates, frees or
+ *     synchronises, and keeps no state between calls (thread-safe, reentrant).
+ *   - bf16 tensors are IEEE bfloat16 bit patterns (uint16).
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream);
+ *     calls return before the GPU work finishes.
+ *   - Validation happens on the host before anything is launched.  On any error
+ *     status nothing is launched and no output or workspace byte is touched.
+ *   - A device-side check rejects cu_seqlens that is not non-decreasing from 0 to
+ *     T; the outputs o and ht are then filled with NaN (loudly wrong), since the
+ *     host cannot see device memory without synchronising.
+ */
+#ifndef KDA_MI355X_H
+#define KDA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define KDA_OK                 0
+#define KDA_ERR_INVALID_ARG   -1  /* null/misaligned pointer, bad size, HV % HQK != 0 ...  */
+#define KDA_ERR_UNSUPPORTED   -2  /* K not in {64, 128}, V not a multiple of 16           */
+#define KDA_ERR_WORKSPACE     -3  /* workspace NULL, misaligned or smaller than required  */
+#define KDA_ERR_HIP           -4  /* a HIP launch failed; see kda_strerror                */
+
+/* Chunk length of the chunked form (tokens per chunk). */
+#define KDA_CHUNK 64
+
+typedef struct kda_fwd_args {
+  /* Inputs (device, bf16 unless stated).
+   *   q, k : [B, T, HQK, K]  keys/queries, expected L2-normalised over K by the caller
+   *   v    : [B, T, HV,  V]
+   *   g    : [B, T, HV,  K]  natural-log per-dimension decay, g <= 0
+   *   beta : [B, T, HV]      write strength in [0, 1] (already through a sigmoid)
+   *   h0   : fp32 [N, HV, K, V] initial state per sequence and value head, or NULL
+   *          for a zero initial state.
+   *   cu_seqlens : int64 [N + 1] on the device, or NULL.  NULL = fixed length:
+   *          N = B sequences of T tokens.  Non-NULL = varlen: B must be 1, the N
+   *          sequences are rows [cu[n], cu[n+1]) of the packed row, cu[0] = 0,
+   *          cu[N] = T; each sequence starts from its own h0 and chunks restart at
+   *          every sequence start (lengths need not be multiples of 64; empty
+   *          sequences are allowed and return ht = h0).
+   * Value head h reads q/k head h / (HV / HQK) (consecutive value heads share). */
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* beta;
+  float scale;                 /* usually K^-0.5                                      */
+  const float* h0;
+  const int64_t* cu_seqlens;
+  int32_t B, T, HQK, HV, K, V; /* K in {64, 128}; V a positive multiple of 16         */
+  int32_t N;                   /* number of sequences: == B (fixed) or len(cu) - 1    */
+  /* Outputs (device, caller-allocated).
+   *   o  : bf16 [B, T, HV, V]   every row of every sequence is written
+   *   ht : fp32 [N, HV, K, V]   final state per sequence, or NULL to skip it     */
+  void* o;
+  float* ht;
+  /* Scratch (device, caller-allocated, 256-byte aligned, size from
+   * kda_fwd_workspace_bytes).  Contents on entry do not matter. */
+  void* workspace;
+  size_t workspace_bytes;
+  void* stream;                /* hipStream_t */
+} kda_fwd_args;
+
+/* Workspace size for these arguments (host only, launches nothing).  Only the
+ * shape fields (B, T, HQK, HV, K, V, N, and whether cu_seqlens is NULL) are
+ * read.  Returns KDA_OK and *bytes, or an error status. */
+int kda_fwd_workspace_bytes(const kda_fwd_args* a, size_t* bytes);
+
+/* The whole chunked forward: o (and ht) from q, k, v, g, beta, h0 (kernel-fun
+ * docstring; FlashKDA recurrence phases 3-6).  Equivalent to kda_fwd_intra
+ * followed by kda_fwd_inter on the same stream. */
+int kda_fwd(const kda_fwd_args* a);
+
+/* Intra-chunk stage only (per-dimension gate cumsum, gated Aqk, Akk and its
+ * UT/WY inverse, w, qg, kg; kernel-fun docstring): fills the workspace from
+ * q, k, g, beta (and the varlen chunk table from cu_seqlens).  o, ht, v, h0 are
+ * not read.  Exposed so the two stages can be timed separately. */
+int kda_fwd_intra(const kda_fwd_args* a);
+
+/* Inter-chunk state scan only (kernel-fun docstring: v' = u - w h, o = scale qg h
+ * + Aqk v', h <- diag(exp2 G) h + kg^T v'): reads the workspace written by
+ * kda_fwd_intra with the same arguments, plus v and h0; writes o and ht. */
+int kda_fwd_inter(const kda_fwd_args* a);
+
+/* Debug view of the intra-stage results (after kda_fwd_intra with the same
+ * arguments), unpacked from the workspace's internal layout into plain tensors.
+ * Any output pointer may be NULL to skip it.
+ *   qg   : bf16 [B, T, HV, K]   scale * q * exp(Gam)   (Gam = in-chunk gate cumsum)
+ *   w    : bf16 [B, T, HV, K]   Tm diag(beta) (k * exp(Gam))
+ *   kg   : bf16 [B, T, HV, K]   k * exp(Gam_last - Gam)
+ *   aqk  : bf16 [B, T, HV, 64]  row i of the chunk's Aqk (columns = chunk rows)
+ *   tmb  : bf16 [B, T, HV, 64]  row i of Tm diag(beta), Tm = (I + Akk)^-1
+ *   alpha: fp32 [B, T, HV, K]   exp(Gam_last) of the row's chunk, on every row
+ * Rows of each sequence are written; other memory is untouched. */
+int kda_debug_unpack(const kda_fwd_args* a, void* qg, void* w, void* kg, void* aqk,
+                     void* tmb, float* alpha);
+
+/* Static text for a status code, or for the last HIP error seen by this thread
+ * when status == KDA_ERR_HIP. */
+const char* kda_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_MI355X_H */

@@ -1,0 +1,120 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every
+function ``include/kda.h`` declares, sizes the workspace, and rejects bad
+arguments with the documented status before launching anything."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from gated_delta_rule_chunked_amd import kda as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(K.LIB_PATH):
+        from gated_delta_rule_chunked_amd.build import build
+        build()
+    return K.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kda_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(K.EXPORTED)
+
+
+def test_library_exports_every_declared_function(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", K.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (kda_\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_struct_layout_matches_header():
+    # compile-free check of the ctypes mirror: pointer fields 8-aligned, size a multiple of 8
+    a = K.KdaFwdArgs
+    assert a.scale.offset == 40 and a.h0.offset == 48 and a.cu_seqlens.offset == 56
+    assert a.B.offset == 64 and a.N.offset == 88 and a.o.offset == 96
+    assert a.workspace_bytes.offset == 120 and a.stream.offset == 128 and ctypes.sizeof(a) == 136
+
+
+def args(**over):
+    a = K.KdaFwdArgs()
+    fake = 1 << 20          # aligned, never dereferenced: every call below fails validation
+    a.q = a.k = a.v = a.g = a.beta = fake
+    a.o = a.workspace = fake
+    a.scale = 0.125
+    a.B, a.T, a.HQK, a.HV, a.K, a.V, a.N = 1, 256, 2, 4, 128, 128, 1
+    a.workspace_bytes = 0
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def ws(a):
+    n = ctypes.c_size_t(0)
+    st = K.load_library().kda_fwd_workspace_bytes(ctypes.byref(a), ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_bytes(lib):
+    # fixed length: B * ceil(T/64) chunks per value head, one record per (chunk, head)
+    st, n = ws(args(B=1, T=8192, HQK=32, HV=32))
+    assert st == 0 and n == 128 * 32 * 61952
+    st, n = ws(args(B=2, T=200, HQK=1, HV=1, K=64, V=64, N=2))
+    assert st == 0 and n == 2 * 4 * 37120
+    # varlen: ceil(T/64) + N chunk capacity plus the 256-byte chunk table
+    st, n = ws(args(B=1, T=1000, HQK=1, HV=2, N=5, cu_seqlens=1 << 20))
+    assert st == 0 and n == 256 + (16 + 5) * 2 * 61952
+    st, n = ws(args(T=0))
+    assert st == 0 and n == 0
+
+
+ALL = ("kda_fwd", "kda_fwd_intra", "kda_fwd_inter")
+INTRA = ("kda_fwd", "kda_fwd_intra")     # entry points that read q, k, g, beta
+INTER = ("kda_fwd", "kda_fwd_inter")     # entry points that read v, o, h0, ht
+
+
+@pytest.mark.parametrize("over,status,entries", [
+    (dict(K=96), K.KDA_ERR_UNSUPPORTED, ALL),
+    (dict(V=40), K.KDA_ERR_UNSUPPORTED, ALL),
+    (dict(V=0), K.KDA_ERR_UNSUPPORTED, ALL),
+    (dict(HQK=3), K.KDA_ERR_INVALID_ARG, ALL),          # HV % HQK != 0
+    (dict(B=0), K.KDA_ERR_INVALID_ARG, ALL),
+    (dict(T=-1), K.KDA_ERR_INVALID_ARG, ALL),
+    (dict(N=2), K.KDA_ERR_INVALID_ARG, ALL),            # fixed length needs N == B
+    (dict(B=2, N=2, cu_seqlens=1 << 20), K.KDA_ERR_INVALID_ARG, ALL),   # varlen needs B == 1
+    (dict(cu_seqlens=(1 << 20) + 4), K.KDA_ERR_INVALID_ARG, ALL),      # misaligned int64
+    (dict(q=0), K.KDA_ERR_INVALID_ARG, INTRA),
+    (dict(beta=(1 << 20) + 1), K.KDA_ERR_INVALID_ARG, INTRA),
+    (dict(v=(1 << 20) + 8), K.KDA_ERR_INVALID_ARG, INTER),   # misaligned
+    (dict(o=0), K.KDA_ERR_INVALID_ARG, INTER),
+    (dict(h0=(1 << 20) + 4), K.KDA_ERR_INVALID_ARG, INTER),
+    (dict(workspace=0), K.KDA_ERR_WORKSPACE, ALL),
+    (dict(workspace_bytes=1000), K.KDA_ERR_WORKSPACE, ALL),
+    (dict(workspace=(1 << 20) + 128, workspace_bytes=1 << 40), K.KDA_ERR_WORKSPACE, ALL),
+    (dict(scale=float("nan"), workspace_bytes=1 << 40), K.KDA_ERR_INVALID_ARG, ALL),
+])
+def test_validation_rejects_before_launch(lib, over, status, entries):
+    a = args(**over)
+    for name in entries:
+        st = getattr(lib, name)(ctypes.byref(a))
+        assert st == status, (name, over, st)
+    assert K.kda_strerror(status)
+
+
+def test_null_args_and_strerror(lib):
+    assert lib.kda_fwd(None) == K.KDA_ERR_INVALID_ARG
+    assert lib.kda_fwd_workspace_bytes(None, None) == K.KDA_ERR_INVALID_ARG
+    assert K.kda_strerror(0) == "ok" and K.kda_strerror(12345) == "unknown status"
