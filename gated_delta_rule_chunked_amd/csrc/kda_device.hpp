@@ -82,10 +82,32 @@ __device__ __forceinline__ int xcd_remap(int b, int grid) {
   return (b & 7) * (grid >> 3) + (b >> 3);
 }
 
+// -------------------------------------------------------------- P-order
+// Every MFMA fragment that contracts over a 32-wide step uses "P-order": lane
+// group g (lanes 16g .. 16g+15) supplies the contraction indices
+//   {4g, 4g+1, 4g+2, 4g+3, 16+4g, 16+4g+1, 16+4g+2, 16+4g+3}   (step-relative)
+// in that register order.  The 16x16 C layout gives lane group g rows 4g .. 4g+3
+// of each 16-row tile, so a result tile pair (rows 0-15 and 16-31 of the step)
+// becomes an A or B fragment without moving data between lanes.
+__device__ __forceinline__ constexpr int pidx(int g, int e) { return 4 * g + (e & 3) + ((e >> 2) << 4); }
+
+// 8 bf16 of a P-order fragment from a bf16 row whose contraction index is
+// contiguous: two 8-byte reads at base + 4g and base + 16 + 4g.
+__device__ __forceinline__ bf16x8 pfrag(const uint16_t* row, int base, int g) {
+  const uint2 lo = *reinterpret_cast<const uint2*>(row + base + 4 * g);
+  const uint2 hi = *reinterpret_cast<const uint2*>(row + base + 16 + 4 * g);
+  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+// Two C-layout tiles (4 floats each) -> one packed P-order fragment.
+__device__ __forceinline__ uint4 pack_pair(const f32x4& lo, const f32x4& hi) {
+  return make_uint4(pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(hi[0], hi[1]), pack2(hi[2], hi[3]));
+}
+
 // ---------------------------------------------------- workspace records
 // One record per (chunk, value head), written by the intra kernel in the exact
 // register-fragment order the inter kernel consumes, so every inter-kernel
-// operand load is one contiguous 1 KiB wave load (16 B per lane).
+// operand load is one contiguous 1 KiB wave load (16 B per lane).  All
+// fragments are in P-order along their contraction index.
 //
 //   QG  : A operand of  O = qg h     [64 x K] bf16, scale folded in
 //   WN  : A operand of  v' = u + (-w) h   [64 x K] bf16 (negated w)
@@ -95,11 +117,11 @@ __device__ __forceinline__ int xcd_remap(int b, int grid) {
 //   ALPHA: exp2(G) per key dimension, fp32 [K]
 //
 // [64 x K] fragments (QG, WN): frag (mb, s), mb = row block 0..3, s = 32-column
-//   step 0..K/32-1; lane l holds row 16mb + l%16, columns 32s + 8(l/16) .. +7.
+//   step 0..K/32-1; lane l holds row 16mb + l%16 and columns 32s + pidx(l/16, e).
 //   byte offset ((mb * K/32 + s) * 64 + l) * 16.
 // KGT fragments: frag (md, s), md = 16-row block of the key dimension 0..K/16-1,
-//   s = 0,1 (token halves); lane l holds d = 16md + l%16, tokens 32s + 8(l/16) ..
-//   +7.  byte offset ((md * 2 + s) * 64 + l) * 16.
+//   s = 0,1 (token halves); lane l holds d = 16md + l%16, tokens 32s + pidx(l/16, e).
+//   byte offset ((md * 2 + s) * 64 + l) * 16.
 // AQK / TMB: lower-triangular 64 x 64, the two all-zero fragments (rows 0..31,
 //   columns 32..63) are not stored: frag index (mb, s) -> {0,1,2,3,4,5} for
 //   (0,0),(1,0),(2,0),(2,1),(3,0),(3,1); lane layout as QG.
@@ -115,6 +137,11 @@ struct Rec {
   static constexpr int BYTES = ALPHA + K * 4;      // 61952 (K=128), 37120 (K=64)
   static_assert(BYTES % 256 == 0, "records stay 256-byte aligned");
 };
+// Records are stored head-major: all chunks of value head hv are contiguous, so
+// the serial scan of one head streams through consecutive memory.
+__device__ __host__ __forceinline__ int64_t rec_index(int hv, int64_t chunk, int64_t max_chunks) {
+  return (int64_t)hv * max_chunks + chunk;
+}
 __device__ __host__ __forceinline__ constexpr int tri_frag(int mb, int s) {
   return mb < 2 ? mb : 2 * mb - 2 + s;   // (0,0)0 (1,0)1 (2,0)2 (2,1)3 (3,0)4 (3,1)5
 }

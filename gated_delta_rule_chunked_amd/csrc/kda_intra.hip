@@ -23,8 +23,12 @@
 // same factors: exp(Gam_i) = X_i exp(mu_I), exp(Gam_last - Gam_i) = Y_i exp(Gam_last - mu_I).
 //
 // Wave I owns rows 16I..16I+15 through the gate and Aqk/Akk phases; lane
-// l = 16g + r holds row 16I + r and key dims 32s + 8g .. +7 (s = 0..K/32-1),
-// which is at once the MFMA A/B fragment layout and the qg record layout.
+// l = 16g + r holds row 16I + r and the P-order key dims 32s + pidx(g, e)
+// (s = 0..K/32-1, e = 0..7), which is at once an MFMA A/B fragment and the qg
+// record layout.  Results leave the MFMA C layout directly as record fragments:
+// Aqk is computed transposed (operands swapped) and w as w^T = kd^T TmB^T, so a
+// lane's accumulator pair already is its P-order fragment; only kg^T and kd^T
+// (contractions over tokens) are transposed through LDS.
 
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
@@ -38,18 +42,14 @@ struct IntraSmem {
   static constexpr int TOT = 0;                         // float [4][K] block gate totals
   static constexpr int TAB = TOT + 4 * K * 4;           // float [14][K] E, F, c tables
   static constexpr int BETA = TAB + 14 * K * 4;         // float [64]
-  static constexpr int KY = BETA + 256;                 // float [4][S][64][8] k*Y fragments
-  static constexpr int KDT = KY + 4 * S * 64 * 8 * 4;   // bf16 [K][TS] (k*exp(Gam))^T
-  static constexpr int KGT = KDT + K * TS * 2;          // bf16 [K][TS] kg^T
-  static constexpr int END0 = KGT + K * TS * 2;
+  static constexpr int KY = BETA + 256;                 // float [3][S][64][8] k*Y, blocks 0..2
+  static constexpr int KY_BYTES = 3 * S * 64 * 8 * 4;
+  static constexpr int KT = KY + KY_BYTES;              // bf16 [K][TS]: kg^T, later (k exp(Gam))^T
+  static constexpr int END0 = KT + K * TS * 2;
   static constexpr int AS = 68;                         // Akk / Tm row stride (fp32)
   static constexpr int AKK_BYTES = 64 * AS * 4;
-  static constexpr int AKK = (K * TS * 2 >= AKK_BYTES) ? KGT : END0;   // reuses kg^T when it fits
-  static constexpr int STG_S = K + 8;                   // staging row stride (bf16)
-  static constexpr int STG = KY;                        // bf16 [64][STG_S], reuses k*Y
-  static_assert(64 * STG_S * 2 <= 4 * S * 64 * 8 * 4, "staging fits in the k*Y area");
-  static_assert(64 * 72 * 2 <= 4 * S * 64 * 8 * 4, "Aqk staging fits in the k*Y area");
-  static constexpr int BYTES = (AKK == KGT) ? END0 : END0 + AKK_BYTES;
+  static constexpr int AKK = (KY_BYTES >= AKK_BYTES) ? KY : END0;   // reuses k*Y when it fits
+  static constexpr int BYTES = (AKK == KY) ? END0 : END0 + AKK_BYTES;
 };
 
 // Row of the transposed [K][64] tiles: 8-token groups are XOR-swizzled by
@@ -125,8 +125,11 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(Params p) {
 }
 
 // ------------------------------------------------------------ intra kernel
+#ifndef KDA_INTRA_OCC
+#define KDA_INTRA_OCC 2   // workgroups per CU the register budget is sized for
+#endif
 template <int K>
-__global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(Params p, int n_items) {
+__global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p, int n_items) {
   using SM = IntraSmem<K>;
   using R = Rec<K>;
   constexpr int S = SM::S;
@@ -135,10 +138,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(Params p, int n_item
   float* sTab = reinterpret_cast<float*>(smem + SM::TAB);
   float* sBeta = reinterpret_cast<float*>(smem + SM::BETA);
   float* sKY = reinterpret_cast<float*>(smem + SM::KY);
-  uint16_t* sKdT = reinterpret_cast<uint16_t*>(smem + SM::KDT);
-  uint16_t* sKgT = reinterpret_cast<uint16_t*>(smem + SM::KGT);
+  uint16_t* sKT = reinterpret_cast<uint16_t*>(smem + SM::KT);
   float* sAkk = reinterpret_cast<float*>(smem + SM::AKK);
-  uint16_t* sStg = reinterpret_cast<uint16_t*>(smem + SM::STG);
 
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   if (item >= n_items) return;
@@ -149,35 +150,43 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(Params p, int n_item
   const int hq = hv / (p.HV / p.HQK);
 
   const int tid = threadIdx.x;
-  const int wv = tid >> 6;        // row block I
+  // wave index via readfirstlane: branches on it stay scalar (an MFMA under a
+  // lane-predicated branch would still write every lane)
+  const int I = __builtin_amdgcn_readfirstlane(tid >> 6);   // this wave's 16-row block
   const int ln = tid & 63;
-  const int r = ln & 15, grp = ln >> 4;
-  const int i = 16 * wv + r;      // this lane's row in the chunk
+  const int r = ln & 15, g = ln >> 4;
+  const int i = 16 * I + r;       // this lane's row in the chunk
   const bool valid = i < cl.L;
   const int64_t tok = (int64_t)cl.b * p.T + cl.row0 + i;
-  uint8_t* rec = p.recs + (gc * p.HV + hv) * (int64_t)R::BYTES;
+  uint8_t* rec = p.recs + rec_index(hv, gc, p.max_chunks) * (int64_t)R::BYTES;
 
-  // ---- phase 1: loads, gate cumsum, factors -----------------------------------
-  float qf[S][8], kf[S][8], gl[S][8];
+  // ---- phase 1: loads (P-order key dims), gate cumsum, factors --------------------
+  // lane dims for step s, element e: d = 32s + pidx(g, e)
+  uint4 uqs[S], uks[S];   // q, k kept packed (bf16) until used
+  float gl[S][8];
+  float bt;
   {
     const uint16_t* qrow = p.q + (tok * p.HQK + hq) * K;
     const uint16_t* krow = p.k + (tok * p.HQK + hq) * K;
     const uint16_t* grow = p.g + (tok * p.HV + hv) * K;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      const int d0 = 32 * s + 8 * grp;
+      const int lo = 32 * s + 4 * g, hi = lo + 16;
       uint4 uq = make_uint4(0, 0, 0, 0), uk = uq, ug = uq;
       if (valid) {
-        uq = *reinterpret_cast<const uint4*>(qrow + d0);
-        uk = *reinterpret_cast<const uint4*>(krow + d0);
-        ug = *reinterpret_cast<const uint4*>(grow + d0);
+        const uint2 q0 = *reinterpret_cast<const uint2*>(qrow + lo), q1 = *reinterpret_cast<const uint2*>(qrow + hi);
+        const uint2 k0 = *reinterpret_cast<const uint2*>(krow + lo), k1 = *reinterpret_cast<const uint2*>(krow + hi);
+        const uint2 g0 = *reinterpret_cast<const uint2*>(grow + lo), g1 = *reinterpret_cast<const uint2*>(grow + hi);
+        uq = make_uint4(q0.x, q0.y, q1.x, q1.y);
+        uk = make_uint4(k0.x, k0.y, k1.x, k1.y);
+        ug = make_uint4(g0.x, g0.y, g1.x, g1.y);
       }
-      unpack8(uq, qf[s]);
-      unpack8(uk, kf[s]);
+      uqs[s] = uq;
+      uks[s] = uk;
       unpack8(ug, gl[s]);
     }
-    const float bt = valid ? bf2f(p.beta[tok * p.HV + hv]) : 0.f;
-    if (grp == 0) sBeta[i] = bt;
+    bt = valid ? bf2f(p.beta[tok * p.HV + hv]) : 0.f;
+    if (g == 0) sBeta[i] = bt;
   }
   // in-block inclusive cumsum over the 16 rows (lanes r = 0..15 of a DPP row)
 #pragma unroll
@@ -188,7 +197,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(Params p, int n_item
 #pragma unroll
     for (int s = 0; s < S; ++s)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sTot[wv * K + 32 * s + 8 * grp + e] = gl[s][e];
+      for (int e = 0; e < 8; ++e) sTot[I * K + 32 * s + pidx(g, e)] = gl[s][e];
   }
   __syncthreads();  // B1: block totals
 
@@ -199,108 +208,157 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(Params p, int n_item
   for (int idx = tid; idx < 14 * K; idx += NTHREADS) {
     const int row = idx / K, d = idx - row * K;
     const float t0 = sTot[d], t1 = sTot[K + d], t2 = sTot[2 * K + d], t3 = sTot[3 * K + d];
-    const float mu[4] = {0.5f * t0, t0 + 0.5f * t1, t0 + t1 + 0.5f * t2, t0 + t1 + t2 + 0.5f * t3};
+    const float m0 = 0.5f * t0, m1 = t0 + 0.5f * t1, m2 = t0 + t1 + 0.5f * t2, m3 = t0 + t1 + t2 + 0.5f * t3;
     const float G = t0 + t1 + t2 + t3;
     float a;
-    if (row < 4) a = mu[row];
-    else if (row < 8) a = G - mu[row - 4];
-    else {
-      const int pr = row - 8;
-      const int I = pr < 1 ? 1 : (pr < 3 ? 2 : 3);
-      const int J = pr - I * (I - 1) / 2;
-      a = mu[I] - mu[J];
+    switch (row) {
+      case 0: a = m0; break;
+      case 1: a = m1; break;
+      case 2: a = m2; break;
+      case 3: a = m3; break;
+      case 4: a = G - m0; break;
+      case 5: a = G - m1; break;
+      case 6: a = G - m2; break;
+      case 7: a = G - m3; break;
+      case 8: a = m1 - m0; break;    // (1,0)
+      case 9: a = m2 - m0; break;    // (2,0)
+      case 10: a = m2 - m1; break;   // (2,1)
+      case 11: a = m3 - m0; break;   // (3,0)
+      case 12: a = m3 - m1; break;   // (3,1)
+      default: a = m3 - m2; break;   // (3,2)
     }
-    sTab[idx] = exp2f(LOG2E * a);
+    sTab[idx] = __builtin_amdgcn_exp2f(LOG2E * a);
   }
   if (tid < K) {
     const int d = tid;
     const float G = sTot[d] + sTot[K + d] + sTot[2 * K + d] + sTot[3 * K + d];
-    reinterpret_cast<float*>(rec + R::ALPHA)[d] = exp2f(LOG2E * G);
+    reinterpret_cast<float*>(rec + R::ALPHA)[d] = __builtin_amdgcn_exp2f(LOG2E * G);
   }
   __syncthreads();  // B2: tables
 
-  bf16x8 QX[S], KX[S];
+  // Transposed [K][TS] tile address of (key dim d, this lane's row i): for the
+  // P-order dims d = 32s + 4g + e (lo half) and 32s + 16 + 4g + e (hi half) the
+  // swizzle depends only on g and the half, so two lane bases plus a constant.
+  const int kt_lo = (4 * g) * SM::TS + tcol(i, 4 * g);
+  const int kt_hi = (16 + 4 * g) * SM::TS + tcol(i, 16 + 4 * g);
+  bf16x8 QX[S], KX[S], KYr[S];
+  uint4 KD[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    float qx[8], kx[8], ky[8], qg[8];
-    const int d0 = 32 * s + 8 * grp;
+    uint2 pq[2], pk[2], py[2], pg[2], pd[2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = d0 + e;
-      const float half = 0.5f * sTot[wv * K + d];
-      const float X = exp2f(LOG2E * (gl[s][e] - half));
-      const float Y = exp2f(LOG2E * (half - gl[s][e]));
-      const float E = sTab[wv * K + d];
-      const float F = sTab[(4 + wv) * K + d];
-      qx[e] = qf[s][e] * X;
-      kx[e] = kf[s][e] * X;
-      ky[e] = kf[s][e] * Y;
-      qg[e] = p.scale * qx[e] * E;
-      sKdT[d * SM::TS + tcol(i, d)] = f2bf(kx[e] * E);
-      sKgT[d * SM::TS + tcol(i, d)] = f2bf(ky[e] * F);
+    for (int hf = 0; hf < 2; ++hf) {
+      const uint2 qw = hf ? make_uint2(uqs[s].z, uqs[s].w) : make_uint2(uqs[s].x, uqs[s].y);
+      const uint2 kw = hf ? make_uint2(uks[s].z, uks[s].w) : make_uint2(uks[s].x, uks[s].y);
+      const float qf[4] = {bflo(qw.x), bfhi(qw.x), bflo(qw.y), bfhi(qw.y)};
+      const float kf[4] = {bflo(kw.x), bfhi(kw.x), bflo(kw.y), bfhi(kw.y)};
+      float qx[4], kx[4], ky[4], qg[4], kd[4];
+      const int d0 = 32 * s + 16 * hf + 4 * g;   // 4 consecutive key dims
+      const float4 tot4 = *reinterpret_cast<const float4*>(sTot + I * K + d0);
+      const float4 E4 = *reinterpret_cast<const float4*>(sTab + I * K + d0);
+      const float4 F4 = *reinterpret_cast<const float4*>(sTab + (4 + I) * K + d0);
+      const float tot[4] = {tot4.x, tot4.y, tot4.z, tot4.w};
+      const float Ev[4] = {E4.x, E4.y, E4.z, E4.w};
+      const float Fv[4] = {F4.x, F4.y, F4.z, F4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = gl[s][4 * hf + e] - 0.5f * tot[e];
+        const float X = __builtin_amdgcn_exp2f(LOG2E * x);
+        const float Y = __builtin_amdgcn_exp2f(-LOG2E * x);
+        qx[e] = qf[e] * X;
+        kx[e] = kf[e] * X;
+        ky[e] = kf[e] * Y;
+        qg[e] = p.scale * qx[e] * Ev[e];
+        kd[e] = kx[e] * Ev[e];
+        sKT[(hf ? kt_hi : kt_lo) + (32 * s + e) * SM::TS] = f2bf(ky[e] * Fv[e]);   // kg^T
+      }
+      pq[hf] = make_uint2(pack2(qx[0], qx[1]), pack2(qx[2], qx[3]));
+      pk[hf] = make_uint2(pack2(kx[0], kx[1]), pack2(kx[2], kx[3]));
+      py[hf] = make_uint2(pack2(ky[0], ky[1]), pack2(ky[2], ky[3]));
+      pg[hf] = make_uint2(pack2(qg[0], qg[1]), pack2(qg[2], qg[3]));
+      pd[hf] = make_uint2(pack2(kd[0], kd[1]), pack2(kd[2], kd[3]));
+      if (I < 3)
+        reinterpret_cast<float4*>(sKY + ((I * S + s) * 64 + ln) * 8)[hf] = make_float4(ky[0], ky[1], ky[2], ky[3]);
     }
-    QX[s] = as_frag(pack8(qx));
-    KX[s] = as_frag(pack8(kx));
-    float4* dst = reinterpret_cast<float4*>(sKY + ((wv * S + s) * 64 + ln) * 8);
-    dst[0] = make_float4(ky[0], ky[1], ky[2], ky[3]);
-    dst[1] = make_float4(ky[4], ky[5], ky[6], ky[7]);
-    *reinterpret_cast<uint4*>(rec + R::QG + ((wv * S + s) * 64 + ln) * 16) = pack8(qg);
+    QX[s] = as_frag(make_uint4(pq[0].x, pq[0].y, pq[1].x, pq[1].y));
+    KX[s] = as_frag(make_uint4(pk[0].x, pk[0].y, pk[1].x, pk[1].y));
+    KYr[s] = as_frag(make_uint4(py[0].x, py[0].y, py[1].x, py[1].y));
+    KD[s] = make_uint4(pd[0].x, pd[0].y, pd[1].x, pd[1].y);
+    *reinterpret_cast<uint4*>(rec + R::QG + ((I * S + s) * 64 + ln) * 16) =
+        make_uint4(pg[0].x, pg[0].y, pg[1].x, pg[1].y);
   }
-  __syncthreads();  // B3: k*Y, kd^T, kg^T
+  __syncthreads();  // B3: k*Y blocks, kg^T
 
-  // ---- phase 2: kg^T record, Aqk / Akk block row I = wv --------------------------
-  for (int f = wv; f < 2 * (K / 16); f += 4) {
+  // ---- phase 2: kg^T record; (k exp(Gam))^T; transposed Aqk / Akk of block row I --
+  for (int f = I; f < 2 * (K / 16); f += 4) {
     const int md = f >> 1, s2 = f & 1;
     const int d = 16 * md + r;
-    const uint4 u = *reinterpret_cast<const uint4*>(sKgT + d * SM::TS + tcol(32 * s2 + 8 * grp, d));
-    *reinterpret_cast<uint4*>(rec + R::KGT + (f * 64 + ln) * 16) = u;
+    const uint16_t* row = sKT + d * SM::TS;
+    const uint2 lo = *reinterpret_cast<const uint2*>(row + tcol(32 * s2 + 4 * g, d));
+    const uint2 hi = *reinterpret_cast<const uint2*>(row + tcol(32 * s2 + 16 + 4 * g, d));
+    *reinterpret_cast<uint4*>(rec + R::KGT + (f * 64 + ln) * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
   }
-  f32x4 aq[4], ak[4];
+  __syncthreads();  // B4: every read of kg^T is done
 #pragma unroll
-  for (int J = 0; J < 4; ++J) {
-    aq[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-    ak[J] = aq[J];
-    if (J > wv) continue;
-    const int pr = 8 + wv * (wv - 1) / 2 + J;   // c_IJ table row (J < I)
+  for (int s = 0; s < S; ++s) {
+    const uint32_t wd[4] = {KD[s].x, KD[s].y, KD[s].z, KD[s].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint16_t v = (uint16_t)((wd[e >> 1] >> (16 * (e & 1))) & 0xffff);
+      sKT[(e < 4 ? kt_lo : kt_hi) + (32 * s + (e & 3)) * SM::TS] = v;   // (k exp(Gam))^T
+    }
+  }
+  // C = (k Y c) (q X)^T: lane holds [j = 16J + 4g + rr][i = 16I + r], i.e. row i of
+  // Aqk / Akk at columns 16J + 4g + rr -- already the P-order A fragment of the
+  // inter kernel's Aqk v' product.  Block J = I uses this wave's own k*Y.
+  auto block = [&](int J, f32x4& aq, f32x4& ak) {
+    aq = f32x4{0.f, 0.f, 0.f, 0.f};
+    ak = aq;
+    if (J > I) return;
+    const int pr = 8 + I * (I - 1) / 2 + J;   // c_IJ table row (J < I)
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      const float4* src = reinterpret_cast<const float4*>(sKY + ((J * S + s) * 64 + ln) * 8);
-      const float4 a0 = src[0], a1 = src[1];
-      float b[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      if (J < wv) {
-        const float4* c = reinterpret_cast<const float4*>(sTab + pr * K + 32 * s + 8 * grp);
-        const float4 c0 = c[0], c1 = c[1];
-        b[0] *= c0.x; b[1] *= c0.y; b[2] *= c0.z; b[3] *= c0.w;
-        b[4] *= c1.x; b[5] *= c1.y; b[6] *= c1.z; b[7] *= c1.w;
+      bf16x8 A;
+      if (J == I) {
+        A = KYr[s];
+      } else {
+        const float4* src = reinterpret_cast<const float4*>(sKY + ((J * S + s) * 64 + ln) * 8);
+        const float4 a0 = src[0], a1 = src[1];
+        const float* c = sTab + pr * K + 32 * s;
+        const float4 c0 = *reinterpret_cast<const float4*>(c + 4 * g);
+        const float4 c1 = *reinterpret_cast<const float4*>(c + 16 + 4 * g);
+        const float b[8] = {a0.x * c0.x, a0.y * c0.y, a0.z * c0.z, a0.w * c0.w,
+                            a1.x * c1.x, a1.y * c1.y, a1.z * c1.z, a1.w * c1.w};
+        A = as_frag(pack8(b));
       }
-      const bf16x8 B = as_frag(pack8(b));
-      aq[J] = mfma16x32(QX[s], B, aq[J]);
-      ak[J] = mfma16x32(KX[s], B, ak[J]);
+      aq = mfma16x32(A, QX[s], aq);
+      ak = mfma16x32(A, KX[s], ak);
     }
-  }
-  __syncthreads();  // B4: k*Y and kg^T reads done (their space is reused below)
-
-  // Akk -> LDS fp32 (full 64 columns of this block row, zeros right of the block
-  // diagonal); Aqk -> staging bf16.  C layout: rows 16I + 4grp + rr, column 16J + r.
+  };
+  f32x4 vk[4];
 #pragma unroll
-  for (int J = 0; J < 4; ++J) {
+  for (int s2 = 0; s2 < 2; ++s2) {
+    f32x4 vq[2];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int row = 16 * wv + 4 * grp + rr, col = 16 * J + r;
-      float vk = 0.f, vq = 0.f;
-      if (J < wv || (J == wv && col < row)) vk = sBeta[row] * ak[J][rr];
-      if (J < wv || (J == wv && col <= row)) vq = p.scale * aq[J][rr];
-      sAkk[row * SM::AS + col] = vk;
-      sStg[row * 72 + col] = f2bf(vq);
+    for (int h = 0; h < 2; ++h) {
+      const int J = 2 * s2 + h;
+      f32x4 aq, ak;
+      block(J, aq, ak);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int j = 4 * g + rr;   // column within block J
+        vq[h][rr] = (J < I || (J == I && j <= r)) ? p.scale * aq[rr] : 0.f;
+        vk[J][rr] = (J < I || (J == I && j < r)) ? bt * ak[rr] : 0.f;
+      }
     }
+    if (s2 < tri_steps(I))
+      *reinterpret_cast<uint4*>(rec + R::AQK + (tri_frag(I, s2) * 64 + ln) * 16) = pack_pair(vq[0], vq[1]);
   }
-  __syncthreads();  // B5
-
-  // Aqk record fragments (this wave's row block)
-  for (int s2 = 0; s2 < tri_steps(wv); ++s2) {
-    const uint4 u = *reinterpret_cast<const uint4*>(sStg + (16 * wv + r) * 72 + 32 * s2 + 8 * grp);
-    *reinterpret_cast<uint4*>(rec + R::AQK + (tri_frag(wv, s2) * 64 + ln) * 16) = u;
-  }
+  __syncthreads();  // B5: every read of k*Y is done (Akk reuses its space)
+#pragma unroll
+  for (int J = 0; J < 4; ++J)
+    *reinterpret_cast<float4*>(sAkk + i * SM::AS + 16 * J + 4 * g) = make_float4(vk[J][0], vk[J][1], vk[J][2], vk[J][3]);
+  __syncthreads();  // B6: Akk and (k exp(Gam))^T complete
 
   // ---- phase 3: Tm = (I + Akk)^-1 ------------------------------------------------
   // 3a: inverse of the unit lower diagonal block I, one column (r) per lane, by
@@ -309,7 +367,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(Params p, int n_item
     float x[16];
 #pragma unroll
     for (int m = 0; m < 16; ++m) x[m] = (m == r) ? 1.f : 0.f;
-    const float* A = sAkk + (16 * wv) * SM::AS + 16 * wv;
+    const float* A = sAkk + (16 * I) * SM::AS + 16 * I;
 #pragma unroll
     for (int ii = 1; ii < 16; ++ii) {
       float acc = 0.f;
@@ -317,91 +375,92 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(Params p, int n_item
       for (int m = 0; m < ii; ++m) acc += A[ii * SM::AS + m] * x[m];
       if (ii > r) x[ii] = -acc;
     }
-    if (grp == 0) {
-      float* Aw = sAkk + (16 * wv) * SM::AS + 16 * wv;
+    if (g == 0) {
+      float* Aw = sAkk + (16 * I) * SM::AS + 16 * I;
 #pragma unroll
       for (int ii = 0; ii < 16; ++ii) Aw[ii * SM::AS + r] = x[ii];
     }
   }
-  __syncthreads();  // B6: diagonal blocks hold D_I
+  __syncthreads();  // B7: diagonal blocks hold D_I
 
-  // 3b: block column J = wv below the diagonal:
-  //     Inv_IJ = -D_I sum_{J<=M<I} A_IM Inv_MJ   (Inv_JJ = D_J),
+  // 3b: block column J = I below the diagonal:
+  //     Inv_MJ = -D_M sum_{J<=P<M} A_MP Inv_PJ   (Inv_JJ = D_J),
   //     16x16x16 products as four fp32 MFMAs; step kb takes contraction index
-  //     4*grp + kb in lane group grp, so a C-layout result feeds the next
-  //     product's B operand straight from its registers.
+  //     4g + kb in lane group g, so a C-layout result feeds the next product's B
+  //     operand straight from its registers.
   f32x4 inv[4];
 #pragma unroll
-  for (int I = 0; I < 4; ++I) inv[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int M = 0; M < 4; ++M) inv[M] = f32x4{0.f, 0.f, 0.f, 0.f};
   {
-    const int J = wv;
+    const int J = I;
 #pragma unroll
-    for (int I = 1; I < 4; ++I) {
-      if (I <= J) continue;
+    for (int M = 1; M < 4; ++M) {
+      if (M <= J) continue;
       f32x4 P = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int M = 0; M < 3; ++M) {
-        if (M < J || M >= I) continue;
+      for (int Q = 0; Q < 3; ++Q) {
+        if (Q < J || Q >= M) continue;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          const float a = sAkk[(16 * I + r) * SM::AS + 16 * M + 4 * grp + kb];
-          const float b = (M == J) ? sAkk[(16 * J + 4 * grp + kb) * SM::AS + 16 * J + r] : inv[M][kb];
+          const float a = sAkk[(16 * M + r) * SM::AS + 16 * Q + 4 * g + kb];
+          const float b = (Q == J) ? sAkk[(16 * J + 4 * g + kb) * SM::AS + 16 * J + r] : inv[Q][kb];
           P = mfma16x4f32(a, b, P);
         }
       }
-      f32x4 Q = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 D = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const float a = sAkk[(16 * I + r) * SM::AS + 16 * I + 4 * grp + kb];
-        Q = mfma16x4f32(a, P[kb], Q);
+        const float a = sAkk[(16 * M + r) * SM::AS + 16 * M + 4 * g + kb];
+        D = mfma16x4f32(a, P[kb], D);
       }
-      inv[I] = -Q;
+      inv[M] = -D;
     }
   }
-  __syncthreads();  // B7: every read of the Akk blocks is done
-  {
-    const int J = wv;
+  __syncthreads();  // B8: every read of the Akk blocks is done
 #pragma unroll
-    for (int I = 1; I < 4; ++I) {
-      if (I <= J) continue;
+  for (int M = 1; M < 4; ++M) {
+    if (M <= I) continue;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) sAkk[(16 * I + 4 * grp + rr) * SM::AS + 16 * J + r] = inv[I][rr];
-    }
+    for (int rr = 0; rr < 4; ++rr) sAkk[(16 * M + 4 * g + rr) * SM::AS + 16 * I + r] = inv[M][rr];
   }
-  __syncthreads();  // B8: Tm complete
+  __syncthreads();  // B9: Tm complete
 
-  // ---- phase 4: TmB = Tm diag(beta) record fragments; w = TmB (k exp(Gam)) -------
+  // ---- phase 4: TmB = Tm diag(beta) fragments; w^T = (k exp(Gam))^T TmB^T ----------
   bf16x8 TB[2];
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2) {
-    if (s2 >= tri_steps(wv)) continue;
-    const int row = 16 * wv + r, c0 = 32 * s2 + 8 * grp;
-    float t[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) t[e] = sAkk[row * SM::AS + c0 + e] * sBeta[c0 + e];
+    if (s2 >= tri_steps(I)) continue;
+    const float* trow = sAkk + i * SM::AS + 32 * s2;
+    const float* brow = sBeta + 32 * s2;
+    const float4 t0 = *reinterpret_cast<const float4*>(trow + 4 * g);
+    const float4 t1 = *reinterpret_cast<const float4*>(trow + 16 + 4 * g);
+    const float4 b0 = *reinterpret_cast<const float4*>(brow + 4 * g);
+    const float4 b1 = *reinterpret_cast<const float4*>(brow + 16 + 4 * g);
+    const float t[8] = {t0.x * b0.x, t0.y * b0.y, t0.z * b0.z, t0.w * b0.w,
+                        t1.x * b1.x, t1.y * b1.y, t1.z * b1.z, t1.w * b1.w};
     const uint4 u = pack8(t);
     TB[s2] = as_frag(u);
-    *reinterpret_cast<uint4*>(rec + R::TMB + (tri_frag(wv, s2) * 64 + ln) * 16) = u;
+    *reinterpret_cast<uint4*>(rec + R::TMB + (tri_frag(I, s2) * 64 + ln) * 16) = u;
   }
-#pragma unroll
-  for (int nt = 0; nt < K / 16; ++nt) {
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int d = 16 * nt + r;
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      if (s2 >= tri_steps(wv)) continue;
-      const uint4 u = *reinterpret_cast<const uint4*>(sKdT + d * SM::TS + tcol(32 * s2 + 8 * grp, d));
-      acc = mfma16x32(TB[s2], as_frag(u), acc);
-    }
-    // stage -w, C layout: row 16I + 4grp + rr, column d
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) sStg[(16 * wv + 4 * grp + rr) * SM::STG_S + d] = f2bf(-acc[rr]);
-  }
-  __syncthreads();  // B9
+  // C[d][t] = sum_t' kd[t'][d] TmB[t][t'] = w[t][d]: lane holds w row 16I + r at
+  // key dims 16md + 4g + rr, so tile pairs (md = 2s, 2s+1) form WN fragment (I, s).
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    const uint4 u = *reinterpret_cast<const uint4*>(sStg + (16 * wv + r) * SM::STG_S + 32 * s + 8 * grp);
-    *reinterpret_cast<uint4*>(rec + R::WN + ((wv * S + s) * 64 + ln) * 16) = u;
+    f32x4 acc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int d = 16 * (2 * s + h) + r;
+      acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        if (s2 >= tri_steps(I)) continue;
+        const uint16_t* row = sKT + d * SM::TS;
+        const uint2 lo = *reinterpret_cast<const uint2*>(row + tcol(32 * s2 + 4 * g, d));
+        const uint2 hi = *reinterpret_cast<const uint2*>(row + tcol(32 * s2 + 16 + 4 * g, d));
+        acc[h] = mfma16x32(as_frag(make_uint4(lo.x, lo.y, hi.x, hi.y)), TB[s2], acc[h]);
+      }
+    }
+    *reinterpret_cast<uint4*>(rec + R::WN + ((I * S + s) * 64 + ln) * 16) = pack_pair(-acc[0], -acc[1]);
   }
 }
 
@@ -419,42 +478,47 @@ __global__ __launch_bounds__(NTHREADS) void unpack_kernel(Params p, int n_items,
   const int64_t gc = item / p.HV;
   ChunkLoc cl;
   if (!locate_chunk(p, gc, cl)) return;
-  const uint8_t* rec = p.recs + (gc * p.HV + hv) * (int64_t)R::BYTES;
-  const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, r = ln & 15, grp = ln >> 4;
+  const uint8_t* rec = p.recs + rec_index(hv, gc, p.max_chunks) * (int64_t)R::BYTES;
+  const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, r = ln & 15, g = ln >> 4;
   auto tokrow = [&](int t) { return ((int64_t)cl.b * p.T + cl.row0 + t) * p.HV + hv; };
   const int t = 16 * wv + r;
   for (int s = 0; s < S; ++s) {
-    const int d0 = 32 * s + 8 * grp;
-    if (t < cl.L) {
-      const uint4 uq = *reinterpret_cast<const uint4*>(rec + R::QG + ((wv * S + s) * 64 + ln) * 16);
-      uint4 uw = *reinterpret_cast<const uint4*>(rec + R::WN + ((wv * S + s) * 64 + ln) * 16);
-      uw.x ^= 0x80008000u; uw.y ^= 0x80008000u; uw.z ^= 0x80008000u; uw.w ^= 0x80008000u;
-      if (qg) *reinterpret_cast<uint4*>(qg + tokrow(t) * K + d0) = uq;
-      if (w) *reinterpret_cast<uint4*>(w + tokrow(t) * K + d0) = uw;
-    }
+    const uint4 uq = *reinterpret_cast<const uint4*>(rec + R::QG + ((wv * S + s) * 64 + ln) * 16);
+    const uint4 uw = *reinterpret_cast<const uint4*>(rec + R::WN + ((wv * S + s) * 64 + ln) * 16);
+    const uint16_t* eq = reinterpret_cast<const uint16_t*>(&uq);
+    const uint16_t* ew = reinterpret_cast<const uint16_t*>(&uw);
+    if (t < cl.L)
+      for (int e = 0; e < 8; ++e) {
+        const int d = 32 * s + pidx(g, e);
+        if (qg) qg[tokrow(t) * K + d] = eq[e];
+        if (w) w[tokrow(t) * K + d] = ew[e] ^ 0x8000;
+      }
   }
-  // kg^T fragments (md, s2): d = 16md + r, tokens 32s2 + 8grp .. +7
+  // kg^T fragments (md, s2): d = 16md + r, tokens 32s2 + pidx(g, e)
   for (int f = wv; f < 2 * (K / 16); f += 4) {
     const int md = f >> 1, s2 = f & 1;
     const uint4 u = *reinterpret_cast<const uint4*>(rec + R::KGT + (f * 64 + ln) * 16);
     const uint16_t* e = reinterpret_cast<const uint16_t*>(&u);
     for (int j = 0; j < 8; ++j) {
-      const int tt = 32 * s2 + 8 * grp + j;
+      const int tt = 32 * s2 + pidx(g, j);
       if (kg && tt < cl.L) kg[tokrow(tt) * K + 16 * md + r] = e[j];
     }
   }
   // triangular 64 x 64: zero fragments are not stored
   for (int s2 = 0; s2 < 2; ++s2) {
-    const int c0 = 32 * s2 + 8 * grp;
     uint4 ua = make_uint4(0, 0, 0, 0), ut = ua;
     if (s2 < tri_steps(wv)) {
       ua = *reinterpret_cast<const uint4*>(rec + R::AQK + (tri_frag(wv, s2) * 64 + ln) * 16);
       ut = *reinterpret_cast<const uint4*>(rec + R::TMB + (tri_frag(wv, s2) * 64 + ln) * 16);
     }
-    if (t < cl.L) {
-      if (aqk) *reinterpret_cast<uint4*>(aqk + tokrow(t) * 64 + c0) = ua;
-      if (tmb) *reinterpret_cast<uint4*>(tmb + tokrow(t) * 64 + c0) = ut;
-    }
+    const uint16_t* ea = reinterpret_cast<const uint16_t*>(&ua);
+    const uint16_t* et = reinterpret_cast<const uint16_t*>(&ut);
+    if (t < cl.L)
+      for (int e = 0; e < 8; ++e) {
+        const int c = 32 * s2 + pidx(g, e);
+        if (aqk) aqk[tokrow(t) * 64 + c] = ea[e];
+        if (tmb) tmb[tokrow(t) * 64 + c] = et[e];
+      }
   }
   if (alpha) {
     const float* al = reinterpret_cast<const float*>(rec + R::ALPHA);
