@@ -59,7 +59,7 @@ int check_call(const kda_fwd_args* a, int need, kda::Params* p) {
   }
   if (need & NEED_INTER) {
     if (any_tokens && (!a->v || !a->o)) return KDA_ERR_INVALID_ARG;
-    if (!aligned(a->v, 16) || !aligned(a->o, 2) || !aligned(a->h0, 16) || !aligned(a->ht, 16))
+    if (!aligned(a->v, 16) || !aligned(a->o, 8) || !aligned(a->h0, 16) || !aligned(a->ht, 16))
       return KDA_ERR_INVALID_ARG;
   }
   if (!aligned(a->cu_seqlens, 8)) return KDA_ERR_INVALID_ARG;

@@ -105,16 +105,18 @@ __device__ __forceinline__ uint4 pack_pair(const f32x4& lo, const f32x4& hi) {
 
 // ---------------------------------------------------- workspace records
 // One record per (chunk, value head), written by the intra kernel in the exact
-// register-fragment order the inter kernel consumes, so every inter-kernel
-// operand load is one contiguous 1 KiB wave load (16 B per lane).  All
-// fragments are in P-order along their contraction index.
+// register-fragment order the inter kernel consumes (64 lanes x 16 B per
+// fragment, so every operand fragment is one contiguous 1 KiB).  All fragments
+// are in P-order along their contraction index.
 //
-//   QG  : A operand of  O = qg h     [64 x K] bf16, scale folded in
 //   WN  : A operand of  v' = u + (-w) h   [64 x K] bf16 (negated w)
 //   KGT : A operand of  DH = kg^T v'  [K x 64] bf16
-//   AQK : A operand of  O += Aqk v'   [64 x 64] bf16 lower triangle
 //   TMB : A operand of  u = (Tm diag beta) v   [64 x 64] bf16 lower triangle
 //   ALPHA: exp2(G) per key dimension, fp32 [K]
+//   QG  : A operand of  O = qg h     [64 x K] bf16, scale folded in
+//   AQK : A operand of  O += Aqk v'   [64 x 64] bf16 lower triangle
+// The state-update operands (WN, KGT, TMB, ALPHA) come first and are contiguous
+// (STATE_BYTES), so the scan stages them into LDS as one block copy.
 //
 // [64 x K] fragments (QG, WN): frag (mb, s), mb = row block 0..3, s = 32-column
 //   step 0..K/32-1; lane l holds row 16mb + l%16 and columns 32s + pidx(l/16, e).
@@ -125,17 +127,20 @@ __device__ __forceinline__ uint4 pack_pair(const f32x4& lo, const f32x4& hi) {
 // AQK / TMB: lower-triangular 64 x 64, the two all-zero fragments (rows 0..31,
 //   columns 32..63) are not stored: frag index (mb, s) -> {0,1,2,3,4,5} for
 //   (0,0),(1,0),(2,0),(2,1),(3,0),(3,1); lane layout as QG.
+// A P-order 32-step fragment is also two 16x16x16 fragments: its low 8 bytes
+// cover indices 4g..4g+3 of the first 16, its high 8 bytes those of the second.
 template <int K>
 struct Rec {
   static constexpr int S = K / 32;                 // 32-wide K steps
-  static constexpr int QG = 0;
-  static constexpr int WN = QG + BT * K * 2;
+  static constexpr int WN = 0;
   static constexpr int KGT = WN + BT * K * 2;
-  static constexpr int AQK = KGT + BT * K * 2;
-  static constexpr int TMB = AQK + 6 * 1024;
+  static constexpr int TMB = KGT + BT * K * 2;
   static constexpr int ALPHA = TMB + 6 * 1024;
-  static constexpr int BYTES = ALPHA + K * 4;      // 61952 (K=128), 37120 (K=64)
-  static_assert(BYTES % 256 == 0, "records stay 256-byte aligned");
+  static constexpr int STATE_BYTES = ALPHA + K * 4;   // 39424 (K=128), 22784 (K=64)
+  static constexpr int QG = STATE_BYTES;
+  static constexpr int AQK = QG + BT * K * 2;
+  static constexpr int BYTES = AQK + 6 * 1024;     // 61952 (K=128), 37120 (K=64)
+  static_assert(BYTES % 256 == 0 && STATE_BYTES % 256 == 0, "records stay 256-byte aligned");
 };
 // Records are stored head-major: all chunks of value head hv are contiguous, so
 // the serial scan of one head streams through consecutive memory.

@@ -8,20 +8,25 @@
 //   o   = qg h + Aqk v'              (scale already folded into qg and Aqk)
 //   h  <- diag(exp2 G) h + kg^T v'   (fp32; the decay is the MFMA's C input)
 //
-// Eight waves in two roles, as the kernel-fun design keeps the o readout off the
-// recurrence's critical path:
-//   waves 0-3 (state waves): wave w owns key rows [w K/4, (w+1) K/4) of h in the
-//     C layout of the kg^T v' MFMA (the update never leaves registers), and rows
-//     16w..16w+15 of u, w h and v'.
-//   waves 4-7 (output waves): rows 16(w-4).. of qg h + Aqk v', the o stores, and
-//     the loads of the v tile.
-// The bf16 copy of h (B operand of w h and qg h) and v' (B operand of Aqk v' and
-// kg^T v') cross waves through LDS once per chunk; two workgroup barriers per
-// chunk.  All B fragments are read in P-order (kda_device.hpp), exactly as the
-// owner lanes wrote them.
-//
-// Operands are read straight from the workspace records (one 16-byte load per
-// lane per fragment) into per-role register rings several chunks deep.
+// Eight waves in three roles, one workgroup barrier per chunk:
+//   wave 0 (state wave): holds the whole state h in the C layout of 16x16 MFMA
+//     tiles.  A 16x16 C tile is already the B operand of the next product along
+//     its rows (P-order, kda_device.hpp), so u, v' = u + (-w) h and
+//     h <- diag(alpha) h + kg^T v' run back to back in registers, with no LDS
+//     round trip and no barrier inside the recurrence.  It reads its operands
+//     (WN, KGT, TMB, ALPHA, v^T) from LDS in two batches ahead of the products
+//     and publishes the bf16 h and v' of the chunk for the output waves.
+//   waves 1-4 (output waves): o of the previous chunk, o = qg h + Aqk v', from the
+//     published h and v' and their own qg / Aqk fragments (a register ring fed
+//     from the workspace records five phases ahead); they also stage the v tiles
+//     (v^T in LDS).
+//   waves 5-7 (loader waves): keep the state operands of three chunks in flight in
+//     a register ring (plain 16-byte loads, the record read as 1 KiB steps) and
+//     write chunk c+1 into the free slot of a two-slot LDS ring during phase c.
+// Phase p (between barriers p-1 and p): the state wave runs chunk p, the output
+// waves finish chunk p-1 and store the v tile of chunk p+1, the loaders stage
+// chunk p+1 and fetch chunk p+3.  The barrier is a raw s_barrier after the wave's
+// own LDS writes, so no wave waits for its outstanding global loads there.
 
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
@@ -29,22 +34,33 @@
 namespace kda {
 
 constexpr int INTER_THREADS = 512;
+constexpr int LD_RING = 3;     // chunks of state operands in flight per loader wave
+constexpr int OUT_RING = 6;    // output-wave operand ring (phases); a multiple of LD_RING
 
 template <int K>
-struct StateOps {                          // state-wave operands of one chunk
-  static constexpr int S = K / 32;
-  static constexpr int MT = K / 64;
-  uint4 wn[S];
-  uint4 tmb[2];
-  uint4 kgt[MT][2];
-  float4 alpha[MT];
+struct InterSmem {
+  using R = Rec<K>;
+  static constexpr int NSTEP = (R::STATE_BYTES + 1023) / 1024;  // 1 KiB steps of the state operands
+  static constexpr int NLD = (NSTEP + 2) / 3;                    // steps per loader wave
+  static constexpr int STAGE = NLD * 3 * 1024;                   // one slot of the LDS ring
+  static constexpr int ST = 0;                                   // two slots
+  // published bf16 h (K/16 tiles) and v' (4 tiles) of a chunk, 64 lanes x 8 B per tile
+  static constexpr int HB_BYTES = (K / 16) * 512 + 4 * 512;
+  static constexpr int HB = ST + 2 * STAGE;                      // two buffers
+  static constexpr int VS = BT + 8;                              // v^T row stride (bf16)
+  static constexpr int VT = HB + 2 * HB_BYTES;                   // two v^T tiles
+  static constexpr int BYTES = VT + 2 * BV * VS * 2;
+  static_assert(STAGE <= R::BYTES, "padded copy steps stay inside the record");
+  static_assert(BYTES <= 160 * 1024, "fits the LDS of one CU");
+  static_assert(OUT_RING % LD_RING == 0, "one phase count serves every role");
 };
+
 template <int K>
-struct OutOps {                            // output-wave operands of one chunk
+struct OutOps {                            // output-wave operands of one phase
   static constexpr int S = K / 32;
-  uint4 qg[S];
+  uint4 qg[S];                             // chunk p-1
   uint4 aqk[2];
-  uint2 v;                                 // 4 columns of one token row of v
+  uint2 v;                                 // chunk p+1: 4 columns of one token row of v
 };
 
 struct SeqLoc {
@@ -59,88 +75,28 @@ __device__ __forceinline__ const uint8_t* rec_ptr(const Params& p, const SeqLoc&
   return p.recs + rec_index(hv, sq.cbase + c, p.max_chunks) * (int64_t)Rec<K>::BYTES;
 }
 
-template <int K>
-__device__ __forceinline__ void load_state_ops(const Params& p, const SeqLoc& sq, int hv, int c, int w, int ln,
-                                               StateOps<K>& op) {
-  using R = Rec<K>;
-  using O = StateOps<K>;
-  const uint8_t* rec = rec_ptr<K>(p, sq, hv, c);
-#pragma unroll
-  for (int s = 0; s < O::S; ++s)
-    op.wn[s] = *reinterpret_cast<const uint4*>(rec + R::WN + ((w * O::S + s) * 64 + ln) * 16);
-#pragma unroll
-  for (int mt = 0; mt < O::MT; ++mt)
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-      op.kgt[mt][s2] = *reinterpret_cast<const uint4*>(rec + R::KGT + (((w * O::MT + mt) * 2 + s2) * 64 + ln) * 16);
-  // row blocks 0, 1 have one nonzero 32-column step; their second load re-reads the
-  // first fragment (unused) so that every load is unconditional
-#pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2)
-    op.tmb[s2] = *reinterpret_cast<const uint4*>(rec + R::TMB + (tri_frag(w, min(s2, tri_steps(w) - 1)) * 64 + ln) * 16);
-  const int g = ln >> 4;
-#pragma unroll
-  for (int mt = 0; mt < O::MT; ++mt)
-    op.alpha[mt] = *reinterpret_cast<const float4*>(rec + R::ALPHA + (w * (K / 4) + 16 * mt + 4 * g) * 4);
-}
+// Raw barrier: the wave's own LDS writes complete, then s_barrier, with a compiler
+// memory clobber.  __syncthreads would also wait for every outstanding global load
+// of the wave, which would serialize the register rings.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int K>
-__device__ __forceinline__ void load_out_ops(const Params& p, const SeqLoc& sq, int hv, int vt, int c, int w,
-                                             int ln, int otid, OutOps<K>& op) {
-  using R = Rec<K>;
-  using O = OutOps<K>;
-  const uint8_t* rec = rec_ptr<K>(p, sq, hv, c);
-#pragma unroll
-  for (int s = 0; s < O::S; ++s)
-    op.qg[s] = *reinterpret_cast<const uint4*>(rec + R::QG + ((w * O::S + s) * 64 + ln) * 16);
-#pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2)   // unconditional, as for TMB
-    op.aqk[s2] = *reinterpret_cast<const uint4*>(rec + R::AQK + (tri_frag(w, min(s2, tri_steps(w) - 1)) * 64 + ln) * 16);
-  // v tile: output thread otid -> token row otid/4, columns 4*(otid%4) .. +3.  The
-  // load is unconditional (rows past the sequence end re-read its last row) so the
-  // number of loads in flight is the same every chunk; store_v_tile zeroes those rows.
-  const int t = min(c * BT + (otid >> 2), sq.len - 1);
-  op.v = *reinterpret_cast<const uint2*>(p.v + (((int64_t)sq.b * p.T + sq.bos + t) * p.HV + hv) * p.V +
-                                         vt * BV + 4 * (otid & 3));
-}
-
-// LDS: bf16 [16 columns][stride] tiles, key/token index contiguous.
-template <int K>
-struct InterSmem {
-  static constexpr int HS = K + 8;      // h^T row stride
-  static constexpr int VS = BT + 8;     // v'^T and v^T row stride
-  static constexpr int H = 0;
-  static constexpr int VP = H + BV * HS * 2;
-  static constexpr int VT = VP + BV * VS * 2;   // two buffers
-  static constexpr int BYTES = VT + 2 * BV * VS * 2;
-};
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint2 pack4(const f32x4& a) {
   return make_uint2(pack2(a[0], a[1]), pack2(a[2], a[3]));
 }
+__device__ __forceinline__ bf16x8 cat(const uint2& lo, const uint2& hi) {
+  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+__device__ __forceinline__ uint2 lds8(const uint8_t* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 template <int K>
-__device__ __forceinline__ void store_v_tile(uint16_t* sVT, int otid, uint2 v, int c, int len) {
-  using SM = InterSmem<K>;
-  const int trow = otid >> 2, c0 = 4 * (otid & 3);
-  if (c * BT + trow >= len) v = make_uint2(0, 0);   // rows past the sequence end
-  sVT[(c0 + 0) * SM::VS + trow] = (uint16_t)(v.x & 0xffff);
-  sVT[(c0 + 1) * SM::VS + trow] = (uint16_t)(v.x >> 16);
-  sVT[(c0 + 2) * SM::VS + trow] = (uint16_t)(v.y & 0xffff);
-  sVT[(c0 + 3) * SM::VS + trow] = (uint16_t)(v.y >> 16);
-}
-
-template <int K, int PFS, int PFO>
 __global__ __launch_bounds__(INTER_THREADS, 1) void inter_kernel(Params p, int n_items) {
-  // Both roles run the same number of iterations (whole ring turns), so every
-  // workgroup barrier is met by all eight waves.
-  static_assert(PFS == PFO, "state and output rings must have the same depth");
   using SM = InterSmem<K>;
-  constexpr int S = K / 32, MT = K / 64;
+  using R = Rec<K>;
+  constexpr int S = K / 32, ND = K / 16, PF = OUT_RING - 1;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SM::BYTES];
-  uint16_t* sH = reinterpret_cast<uint16_t*>(smem + SM::H);
-  uint16_t* sVP = reinterpret_cast<uint16_t*>(smem + SM::VP);
-  uint16_t* sVT = reinterpret_cast<uint16_t*>(smem + SM::VT);
 
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   if (item >= n_items) return;
@@ -152,7 +108,6 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void inter_kernel(Params p, int n
   // The wave index goes through readfirstlane so that every branch on it is a
   // scalar branch: an MFMA under a lane-predicated branch still writes all lanes.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int w = wave & 3;               // row block (and key block for state waves)
 
   SeqLoc sq;
   if (p.cu == nullptr) {
@@ -172,171 +127,230 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void inter_kernel(Params p, int n
     sq.b = 0; sq.bos = p.cu[n]; sq.len = (int)(p.cu[n + 1] - p.cu[n]); sq.cbase = p.table[n];
   }
   const int nc = (sq.len + BT - 1) / BT;
+  // phases 0..nc (the last only finishes o of chunk nc-1), in whole ring turns;
+  // every role runs the same count, one barrier each
+  const int nphase = (nc + 1 + OUT_RING - 1) / OUT_RING * OUT_RING;
 
-  if (wave < 4) {
-    // ======================== state waves ========================
-    const int dbase = w * (K / 4);
-    f32x4 h[MT];
+  if (wave == 0) {
+    // ============================ state wave ============================
+    // h tile md: lane holds h[16md + 4g + rr][vt*16 + r], rr = 0..3
+    f32x4 h[ND];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
+    for (int md = 0; md < ND; ++md)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int d = dbase + 16 * mt + 4 * g + rr;
-        h[mt][rr] = p.h0 ? p.h0[(((int64_t)n * p.HV + hv) * K + d) * p.V + vt * BV + r] : 0.f;
+        const int d = 16 * md + 4 * g + rr;
+        h[md][rr] = p.h0 ? p.h0[(((int64_t)n * p.HV + hv) * K + d) * p.V + vt * BV + r] : 0.f;
       }
-      *reinterpret_cast<uint2*>(sH + r * SM::HS + dbase + 16 * mt + 4 * g) = pack4(h[mt]);
-    }
-    StateOps<K> ring[PFS + 1];
+    barrier_lds();  // S0
+    for (int ph = 0; ph < nphase; ++ph) {
+      if (ph < nc) {
+        const uint8_t* st = smem + SM::ST + (ph & 1) * SM::STAGE;
+        const uint16_t* vrow = reinterpret_cast<const uint16_t*>(smem + SM::VT) + (ph & 1) * BV * SM::VS + r * SM::VS;
+        // batch 1: v^T, TmB, decay, -w (in the order they are consumed)
+        const bf16x8 vb0 = pfrag(vrow, 0, g), vb1 = pfrag(vrow, 32, g);
+        uint4 tm[6], wn[4 * S];
+        float4 al[ND];
 #pragma unroll
-    for (int j = 0; j < PFS; ++j)
-      if (nc > 0) load_state_ops<K>(p, sq, hv, min(j, nc - 1), w, ln, ring[j]);
-    __syncthreads();  // S0: h and the chunk-0 v tile in LDS
-
-    // u = TmB v for chunk c reads the v tile in buffer c & 1, stored by the output
-    // waves before barrier A of chunk c-1 (before S0 for chunk 0); it is computed
-    // off the critical path, after barrier A of the previous chunk.
-    auto tmb_v = [&](const StateOps<K>& op, int c) {
-      const uint16_t* vrow = sVT + (c & 1) * BV * SM::VS + r * SM::VS;
-      const bf16x8 v0 = pfrag(vrow, 0, g), v1 = pfrag(vrow, 32, g);
-      f32x4 u0 = mfma16x32(as_frag(op.tmb[0]), v0, f32x4{0.f, 0.f, 0.f, 0.f});
-      if (tri_steps(w) > 1) u0 = mfma16x32(as_frag(op.tmb[1]), v1, u0);   // scalar branch
-      return u0;
-    };
-    f32x4 u = tmb_v(ring[0], 0);
-
-    // Whole ring turns, no early exit, so every ring slot stays a fixed set of
-    // registers; turns past the last chunk are masked (h kept, nothing stored).
-    const int nturn = (nc + PFS) / (PFS + 1);
-    for (int t0 = 0; t0 < nturn; ++t0) {
+        for (int f = 0; f < 6; ++f) tm[f] = lds16(st + R::TMB + (f * 64 + ln) * 16);
 #pragma unroll
-      for (int j = 0; j <= PFS; ++j) {
-        const int c = t0 * (PFS + 1) + j;
-        const bool active = c < nc;
-        const StateOps<K>& cur = ring[j];
-        // unconditional (clamped) so the count of loads in flight is static
-        load_state_ops<K>(p, sq, hv, min(c + PFS, nc - 1), w, ln, ring[(j + PFS) % (PFS + 1)]);
-        // v' = u + (-w) h  (rows 16w..), two half chains over the key steps
-        bf16x8 hb[S];
+        for (int md = 0; md < ND; ++md) al[md] = *reinterpret_cast<const float4*>(st + R::ALPHA + (16 * md + 4 * g) * 4);
 #pragma unroll
-        for (int s = 0; s < S; ++s) hb[s] = pfrag(sH + r * SM::HS, 32 * s, g);
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) wn[s * 4 + mb] = lds16(st + R::WN + ((mb * S + s) * 64 + ln) * 16);
         __builtin_amdgcn_sched_barrier(0);
-        f32x4 acc = u, acc2 = f32x4{0.f, 0.f, 0.f, 0.f};
+        // u = TmB v, row blocks mb = 0..3 (lower triangular: 1 or 2 32-steps)
+        f32x4 acc[4];
 #pragma unroll
-        for (int s = 0; s < S; s += 2) {
-          acc = mfma16x32(as_frag(cur.wn[s]), hb[s], acc);
-          acc2 = mfma16x32(as_frag(cur.wn[s + 1]), hb[s + 1], acc2);
+        for (int mb = 0; mb < 4; ++mb) {
+          acc[mb] = mfma16x32(as_frag(tm[tri_frag(mb, 0)]), vb0, f32x4{0.f, 0.f, 0.f, 0.f});
+          if (mb >= 2) acc[mb] = mfma16x32(as_frag(tm[tri_frag(mb, 1)]), vb1, acc[mb]);
         }
-        acc += acc2;
-        *reinterpret_cast<uint2*>(sVP + r * SM::VS + 16 * w + 4 * g) = pack4(acc);
-        f32x4 hn[MT];
+        // h as B operand (tiles (2s, 2s+1) form the P-order fragment of 32-step s),
+        // published for the output waves; then h <- diag(alpha) h
+        uint2 hb[ND];
+        uint8_t* hbuf = smem + SM::HB + (ph & 1) * SM::HB_BYTES;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          hn[mt][0] = cur.alpha[mt].x * h[mt][0];
-          hn[mt][1] = cur.alpha[mt].y * h[mt][1];
-          hn[mt][2] = cur.alpha[mt].z * h[mt][2];
-          hn[mt][3] = cur.alpha[mt].w * h[mt][3];
+        for (int md = 0; md < ND; ++md) {
+          hb[md] = pack4(h[md]);
+          *reinterpret_cast<uint2*>(hbuf + (md * 64 + ln) * 8) = hb[md];
+          h[md][0] *= al[md].x;
+          h[md][1] *= al[md].y;
+          h[md][2] *= al[md].z;
+          h[md][3] *= al[md].w;
         }
-        __syncthreads();  // A: v' and v tile c+1 complete; every read of h is done
-        const bf16x8 vb0 = pfrag(sVP + r * SM::VS, 0, g);
-        const bf16x8 vb1 = pfrag(sVP + r * SM::VS, 32, g);
         __builtin_amdgcn_sched_barrier(0);
-        // h <- diag(alpha) h + kg^T v'
+        // batch 2: kg^T
+        uint4 kg[2 * ND];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          hn[mt] = mfma16x32(as_frag(cur.kgt[mt][0]), vb0, hn[mt]);
-          hn[mt] = mfma16x32(as_frag(cur.kgt[mt][1]), vb1, hn[mt]);
-          if (active) h[mt] = hn[mt];
-          *reinterpret_cast<uint2*>(sH + r * SM::HS + dbase + 16 * mt + 4 * g) = pack4(h[mt]);
+        for (int i = 0; i < 2 * ND; ++i) kg[i] = lds16(st + R::KGT + (i * 64 + ln) * 16);
+        __builtin_amdgcn_sched_barrier(0);
+        // v' = u + (-w) h
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          const bf16x8 hbs = cat(hb[2 * s], hb[2 * s + 1]);
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) acc[mb] = mfma16x32(as_frag(wn[s * 4 + mb]), hbs, acc[mb]);
         }
-        u = tmb_v(ring[(j + 1) % (PFS + 1)], c + 1);
-        __syncthreads();  // B: h complete; every read of v' and of v tile c+1 is done
+        uint2 vp[4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          vp[mb] = pack4(acc[mb]);
+          *reinterpret_cast<uint2*>(hbuf + ND * 512 + (mb * 64 + ln) * 8) = vp[mb];
+        }
+        // h <- diag(alpha) h + kg^T v'   (v' tiles (2s2, 2s2+1) = P-order token step s2)
+        const bf16x8 vp0 = cat(vp[0], vp[1]), vp1 = cat(vp[2], vp[3]);
+#pragma unroll
+        for (int md = 0; md < ND; ++md) {
+          h[md] = mfma16x32(as_frag(kg[2 * md]), vp0, h[md]);
+          h[md] = mfma16x32(as_frag(kg[2 * md + 1]), vp1, h[md]);
+        }
       }
+      barrier_lds();
     }
     if (p.ht) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int md = 0; md < ND; ++md)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const int d = dbase + 16 * mt + 4 * g + rr;
-          p.ht[(((int64_t)n * p.HV + hv) * K + d) * p.V + vt * BV + r] = h[mt][rr];
+          const int d = 16 * md + 4 * g + rr;
+          p.ht[(((int64_t)n * p.HV + hv) * K + d) * p.V + vt * BV + r] = h[md][rr];
         }
+    }
+  } else if (wave <= 4) {
+    // ============================ output waves ============================
+    const int w = wave - 1;                 // row block
+    const int otid = tid - 64;              // 0..255 across the four output waves
+    const int trow = otid >> 2, c4 = 4 * (otid & 3);
+    uint16_t* sVT = reinterpret_cast<uint16_t*>(smem + SM::VT);
+    auto v_ptr = [&](int c) {               // row trow of chunk c (clamped into the sequence)
+      const int t = min(c * BT + trow, sq.len - 1);
+      return reinterpret_cast<const uint2*>(p.v + (((int64_t)sq.b * p.T + sq.bos + t) * p.HV + hv) * p.V +
+                                            vt * BV + c4);
+    };
+    auto store_v = [&](int c, uint2 v) {    // v^T tile of chunk c into buffer c & 1; rows past the end are 0
+      if (c * BT + trow >= sq.len) v = make_uint2(0, 0);
+      uint16_t* dst = sVT + (c & 1) * BV * SM::VS;
+      dst[(c4 + 0) * SM::VS + trow] = (uint16_t)(v.x & 0xffff);
+      dst[(c4 + 1) * SM::VS + trow] = (uint16_t)(v.x >> 16);
+      dst[(c4 + 2) * SM::VS + trow] = (uint16_t)(v.y & 0xffff);
+      dst[(c4 + 3) * SM::VS + trow] = (uint16_t)(v.y >> 16);
+    };
+    // ring slot of phase ph: qg / Aqk of chunk ph-1 and v of chunk ph+1 (clamped loads;
+    // unconditional so the number of loads in flight is the same every phase)
+    auto load = [&](int ph, OutOps<K>& op) {
+      const uint8_t* rec = rec_ptr<K>(p, sq, hv, min(max(ph - 1, 0), nc - 1));
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        op.qg[s] = *reinterpret_cast<const uint4*>(rec + R::QG + ((w * S + s) * 64 + ln) * 16);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)   // row blocks 0, 1 have one nonzero step; the second load repeats it
+        op.aqk[s2] = *reinterpret_cast<const uint4*>(rec + R::AQK + (tri_frag(w, min(s2, tri_steps(w) - 1)) * 64 + ln) * 16);
+      op.v = *v_ptr(ph + 1);
+    };
+    if (nc == 0) {                          // empty sequence: only keep the barrier count
+      for (int ph = 0; ph <= nphase; ++ph) barrier_lds();
+      return;
+    }
+    OutOps<K> ring[OUT_RING];
+    const uint2 v0 = *v_ptr(0);
+#pragma unroll
+    for (int j = 0; j < PF; ++j) load(j, ring[j]);
+    store_v(0, v0);
+    barrier_lds();  // S0
+    for (int t0 = 0; t0 < nphase; t0 += OUT_RING) {
+#pragma unroll
+      for (int j = 0; j < OUT_RING; ++j) {
+        const int ph = t0 + j;
+        const OutOps<K>& cur = ring[j];
+        load(ph + PF, ring[(j + PF) % OUT_RING]);
+        if (ph >= 1 && ph <= nc) {
+          const int c = ph - 1;
+          const uint8_t* hbuf = smem + SM::HB + (c & 1) * SM::HB_BYTES;
+          bf16x8 hbs[S];
+#pragma unroll
+          for (int s = 0; s < S; ++s)
+            hbs[s] = cat(lds8(hbuf + ((2 * s) * 64 + ln) * 8), lds8(hbuf + ((2 * s + 1) * 64 + ln) * 8));
+          const bf16x8 vp0 = cat(lds8(hbuf + ND * 512 + (0 * 64 + ln) * 8), lds8(hbuf + ND * 512 + (1 * 64 + ln) * 8));
+          const bf16x8 vp1 = cat(lds8(hbuf + ND * 512 + (2 * 64 + ln) * 8), lds8(hbuf + ND * 512 + (3 * 64 + ln) * 8));
+          // o^T = h^T qg^T + v'^T Aqk^T: the same P-order fragments with A and B
+          // swapped, so lane (g, r) ends up with token 16w + r, columns 4g .. 4g+3
+          // (one 8-byte store per lane instead of four 2-byte ones)
+          f32x4 oacc = f32x4{0.f, 0.f, 0.f, 0.f}, oacc2 = oacc;
+#pragma unroll
+          for (int s = 0; s < S; s += 2) {
+            oacc = mfma16x32(hbs[s], as_frag(cur.qg[s]), oacc);
+            oacc2 = mfma16x32(hbs[s + 1], as_frag(cur.qg[s + 1]), oacc2);
+          }
+          oacc = mfma16x32(vp0, as_frag(cur.aqk[0]), oacc);
+          if (tri_steps(w) > 1) oacc2 = mfma16x32(vp1, as_frag(cur.aqk[1]), oacc2);   // scalar branch
+          oacc += oacc2;
+          const int t = c * BT + 16 * w + r;
+          if (t < sq.len)
+            *reinterpret_cast<uint2*>(p.o + (((int64_t)sq.b * p.T + sq.bos + t) * p.HV + hv) * p.V + vt * BV + 4 * g) =
+                pack4(oacc);
+        }
+        store_v(ph + 1, cur.v);
+        barrier_lds();
+      }
     }
   } else {
-    // ======================== output waves ========================
-    const int otid = tid - 256;
-    OutOps<K> ring[PFO + 1];
-#pragma unroll
-    for (int j = 0; j < PFO; ++j)
-      if (nc > 0) load_out_ops<K>(p, sq, hv, vt, min(j, nc - 1), w, ln, otid, ring[j]);
-    if (nc > 0) store_v_tile<K>(sVT, otid, ring[0].v, 0, sq.len);
-    __syncthreads();  // S0
-
-    // Chunk c's o = qg h + Aqk v' is finished after barrier B (with v' kept in
-    // registers), so the output waves never hold up the state waves between
-    // barriers A and B; its o rows are stored during the next chunk.
-    f32x4 oq = f32x4{0.f, 0.f, 0.f, 0.f};   // qg h of the pending chunk
-    bf16x8 vbp0 = as_frag(make_uint4(0, 0, 0, 0)), vbp1 = vbp0;
-    uint4 aqp0 = make_uint4(0, 0, 0, 0), aqp1 = aqp0;
-    auto finish = [&](int c) {   // o rows 16w + 4g + rr of chunk c, column vt*16 + r
-      f32x4 o0 = mfma16x32(as_frag(aqp0), vbp0, oq);
-      if (tri_steps(w) > 1) o0 = mfma16x32(as_frag(aqp1), vbp1, o0);     // scalar branch
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int t = c * BT + 16 * w + 4 * g + rr;
-        if (t < sq.len)
-          p.o[(((int64_t)sq.b * p.T + sq.bos + t) * p.HV + hv) * p.V + vt * BV + r] = f2bf(o0[rr]);
-      }
-    };
-    const int nturn = (nc + PFO) / (PFO + 1);   // whole ring turns (see the state waves)
-    for (int t0 = 0; t0 < nturn; ++t0) {
-#pragma unroll
-      for (int j = 0; j <= PFO; ++j) {
-        const int c = t0 * (PFO + 1) + j;
-        const OutOps<K>& cur = ring[j];
-        load_out_ops<K>(p, sq, hv, vt, min(c + PFO, nc - 1), w, ln, otid, ring[(j + PFO) % (PFO + 1)]);
-        bf16x8 hb[S];
-#pragma unroll
-        for (int s = 0; s < S; ++s) hb[s] = pfrag(sH + r * SM::HS, 32 * s, g);
-        __builtin_amdgcn_sched_barrier(0);
-        if (c > 0) finish(c - 1);
-        f32x4 oacc = f32x4{0.f, 0.f, 0.f, 0.f}, oacc2 = oacc;
-#pragma unroll
-        for (int s = 0; s < S; s += 2) {
-          oacc = mfma16x32(as_frag(cur.qg[s]), hb[s], oacc);
-          oacc2 = mfma16x32(as_frag(cur.qg[s + 1]), hb[s + 1], oacc2);
-        }
-        oq = oacc + oacc2;
-        aqp0 = cur.aqk[0];
-        aqp1 = tri_steps(w) > 1 ? cur.aqk[1] : make_uint4(0, 0, 0, 0);
-        // next chunk's v tile (rows past the sequence end, or a whole chunk past it, are zeros)
-        store_v_tile<K>(sVT + ((c + 1) & 1) * BV * SM::VS, otid, ring[(j + 1) % (PFO + 1)].v, c + 1, sq.len);
-        __syncthreads();  // A
-        vbp0 = pfrag(sVP + r * SM::VS, 0, g);
-        vbp1 = pfrag(sVP + r * SM::VS, 32, g);
-        __syncthreads();  // B
-      }
+    // ============================ loader waves ============================
+    // Loader wave lw moves 1 KiB steps lw, lw+3, ... of the state operands; chunk c
+    // lives in register slot c % 3 and LDS slot c & 1.
+    constexpr int NLD = SM::NLD;
+    const int lw = wave - 5;
+    if (nc == 0) {                          // empty sequence: only keep the barrier count
+      for (int ph = 0; ph <= nphase; ++ph) barrier_lds();
+      return;
     }
-    const int clast = nturn * (PFO + 1) - 1;   // last iteration's chunk
-    if (clast < nc) finish(clast);             // else it was finished inside the loop
+    auto fetch = [&](int c, u32x4* dst) {   // chunk clamped into the sequence: the tail re-reads it
+      const uint8_t* src = rec_ptr<K>(p, sq, hv, min(c, nc - 1)) + lw * 1024 + ln * 16;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) dst[i] = *reinterpret_cast<const u32x4*>(src + i * 3072);
+    };
+    auto put = [&](int c, const u32x4* src) {
+      uint8_t* dst = smem + SM::ST + (c & 1) * SM::STAGE + lw * 1024 + ln * 16;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) *reinterpret_cast<u32x4*>(dst + i * 3072) = src[i];
+    };
+    // three separately named register slots of native vectors (an array of the
+    // uint4 struct, or a 2-D array, is left in scratch by the compiler)
+    u32x4 ra[NLD], rb[NLD], rc[NLD];
+    fetch(0, ra);
+    fetch(1, rb);
+    fetch(2, rc);
+    put(0, ra);
+    barrier_lds();  // S0: chunk 0 in LDS slot 0
+    static_assert(LD_RING == 3, "the ring turn below is written out for three slots");
+    for (int t0 = 0; t0 < nphase; t0 += LD_RING) {
+      // phase ph: refill the slot of chunk ph (staged during phase ph-1) with chunk
+      // ph+3, then stage chunk ph+1 while the state wave reads LDS slot ph & 1
+      fetch(t0 + 3, ra);
+      __builtin_amdgcn_sched_barrier(0);   // loads issue before the LDS writes
+      put(t0 + 1, rb);
+      barrier_lds();
+      fetch(t0 + 4, rb);
+      __builtin_amdgcn_sched_barrier(0);   // loads issue before the LDS writes
+      put(t0 + 2, rc);
+      barrier_lds();
+      fetch(t0 + 5, rc);
+      __builtin_amdgcn_sched_barrier(0);   // loads issue before the LDS writes
+      put(t0 + 3, ra);
+      barrier_lds();
+    }
   }
 }
-
-#ifndef KDA_INTER_PF
-#define KDA_INTER_PF 3   // chunks in flight ahead of the current one (both roles)
-#endif
-constexpr int INTER_PFS = KDA_INTER_PF;
-constexpr int INTER_PFO = KDA_INTER_PF;
 
 hipError_t launch_inter(const Params& p, hipStream_t s) {
   const int64_t items = (int64_t)p.N * p.HV * (p.V / BV);
   if (items == 0) return hipSuccess;
   const int grid = (int)((items + 7) / 8 * 8);
   if (p.K == 128)
-    hipLaunchKernelGGL((inter_kernel<128, INTER_PFS, INTER_PFO>), dim3(grid), dim3(INTER_THREADS), 0, s, p,
-                       (int)items);
+    hipLaunchKernelGGL((inter_kernel<128>), dim3(grid), dim3(INTER_THREADS), 0, s, p, (int)items);
   else
-    hipLaunchKernelGGL((inter_kernel<64, INTER_PFS, INTER_PFO>), dim3(grid), dim3(INTER_THREADS), 0, s, p,
-                       (int)items);
+    hipLaunchKernelGGL((inter_kernel<64>), dim3(grid), dim3(INTER_THREADS), 0, s, p, (int)items);
   return hipGetLastError();
 }
 

@@ -75,7 +75,9 @@ typedef struct kda_fwd_args {
   int32_t N;                   /* number of sequences: == B (fixed) or len(cu) - 1    */
   /* Outputs (device, caller-allocated).
    *   o  : bf16 [B, T, HV, V]   every row of every sequence is written
-   *   ht : fp32 [N, HV, K, V]   final state per sequence, or NULL to skip it     */
+   *   ht : fp32 [N, HV, K, V]   final state per sequence, or NULL to skip it
+   * Alignment (else KDA_ERR_INVALID_ARG): q, k, v, g, h0, ht 16 bytes; o and
+   * cu_seqlens 8 bytes; beta 2 bytes.  All tensors are dense, row-major.       */
   void* o;
   float* ht;
   /* Scratch (device, caller-allocated, 256-byte aligned, size from

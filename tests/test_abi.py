@@ -100,6 +100,7 @@ INTER = ("kda_fwd", "kda_fwd_inter")     # entry points that read v, o, h0, ht
     (dict(beta=(1 << 20) + 1), K.KDA_ERR_INVALID_ARG, INTRA),
     (dict(v=(1 << 20) + 8), K.KDA_ERR_INVALID_ARG, INTER),   # misaligned
     (dict(o=0), K.KDA_ERR_INVALID_ARG, INTER),
+    (dict(o=(1 << 20) + 4), K.KDA_ERR_INVALID_ARG, INTER),   # o needs 8 bytes
     (dict(h0=(1 << 20) + 4), K.KDA_ERR_INVALID_ARG, INTER),
     (dict(workspace=0), K.KDA_ERR_WORKSPACE, ALL),
     (dict(workspace_bytes=1000), K.KDA_ERR_WORKSPACE, ALL),
