@@ -40,8 +40,9 @@ int check_shapes(const kda_fwd_args* a, kda::WsLayout* L) {
   if (a->N >= (1 << 30)) return KDA_ERR_INVALID_ARG;
   L->rec_bytes = rec_bytes(a->K);
   L->max_chunks = max_chunks;
-  L->table_bytes = a->cu_seqlens ? (((int64_t)a->N + 2) * 4 + 255) / 256 * 256 : 0;
-  L->total_bytes = L->table_bytes + max_chunks * a->HV * L->rec_bytes;
+  const int64_t recs = max_chunks * a->HV * L->rec_bytes;
+  L->table_bytes = recs == 0 ? 0 : (16 + (a->cu_seqlens ? ((int64_t)a->N + 2) * 4 : 0) + 255) / 256 * 256;
+  L->total_bytes = L->table_bytes + recs;
   return KDA_OK;
 }
 
@@ -77,7 +78,8 @@ int check_call(const kda_fwd_args* a, int need, kda::Params* p) {
   p->cu = a->cu_seqlens;
   p->o = (uint16_t*)a->o;
   p->ht = a->ht;
-  p->table = a->cu_seqlens ? (int32_t*)a->workspace : nullptr;
+  p->counter = (int32_t*)a->workspace;
+  p->table = a->cu_seqlens ? (int32_t*)((uint8_t*)a->workspace + 16) : nullptr;
   p->recs = (uint8_t*)a->workspace + L.table_bytes;
   p->scale = a->scale;
   p->B = a->B; p->T = a->T; p->HQK = a->HQK; p->HV = a->HV; p->K = a->K; p->V = a->V; p->N = a->N;
@@ -94,10 +96,9 @@ int hip_status(hipError_t e) {
 }
 
 int run_intra(const kda::Params& p, hipStream_t s) {
-  if (p.cu) {
-    int st = hip_status(kda::launch_chunk_table(p, s));
-    if (st != KDA_OK) return st;
-  }
+  if (p.max_chunks * p.HV == 0) return KDA_OK;
+  int st = hip_status(p.cu ? kda::launch_chunk_table(p, s) : kda::launch_prep(p, s));
+  if (st != KDA_OK) return st;
   return hip_status(kda::launch_intra(p, s));
 }
 

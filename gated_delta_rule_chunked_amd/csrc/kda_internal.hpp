@@ -18,6 +18,7 @@ struct Params {
   uint16_t* o;
   float* ht;
   int32_t* table;        // varlen: chunk_base[N+1], then error flag at [N+1]
+  int32_t* counter;      // work counter of the intra stage (zeroed by the prep kernel)
   uint8_t* recs;         // workspace records
   float scale;
   int B, T, HQK, HV, K, V, N;
@@ -26,7 +27,8 @@ struct Params {
 };
 
 // Host launchers (return the hipError_t of the launch).
-hipError_t launch_chunk_table(const Params& p, hipStream_t s);
+hipError_t launch_chunk_table(const Params& p, hipStream_t s);   // varlen: also zeroes the counter
+hipError_t launch_prep(const Params& p, hipStream_t s);          // fixed length: zeroes the counter
 hipError_t launch_intra(const Params& p, hipStream_t s);
 hipError_t launch_inter(const Params& p, hipStream_t s);
 hipError_t launch_unpack(const Params& p, uint16_t* qg, uint16_t* w, uint16_t* kg,

@@ -33,6 +33,8 @@
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
+#include <algorithm>
+
 namespace kda {
 
 template <int K>
@@ -95,7 +97,10 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(Params p) {
   __shared__ int32_t scan[256];
   __shared__ int32_t bad_any;
   const int tid = threadIdx.x;
-  if (tid == 0) bad_any = (p.cu[0] != 0 || p.cu[p.N] != p.T) ? 1 : 0;
+  if (tid == 0) {
+    bad_any = (p.cu[0] != 0 || p.cu[p.N] != p.T) ? 1 : 0;
+    *p.counter = 0;   // work counter of the intra stage
+  }
   __syncthreads();
   int32_t running = 0;
   for (int base = 0; base < p.N; base += 256) {
@@ -124,6 +129,12 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(Params p) {
   }
 }
 
+// Fixed length: only the intra stage's work counter needs resetting (a kernel
+// rather than a memset, so the sequence can be captured in a graph).
+__global__ void prep_kernel(Params p) {
+  if (threadIdx.x == 0) *p.counter = 0;
+}
+
 // ------------------------------------------------------------ intra kernel
 #ifndef KDA_INTRA_OCC
 #define KDA_INTRA_OCC 2   // workgroups per CU the register budget is sized for
@@ -141,14 +152,6 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
   uint16_t* sKT = reinterpret_cast<uint16_t*>(smem + SM::KT);
   float* sAkk = reinterpret_cast<float*>(smem + SM::AKK);
 
-  const int item = xcd_remap(blockIdx.x, gridDim.x);
-  if (item >= n_items) return;
-  const int hv = item % p.HV;
-  const int64_t gc = item / p.HV;
-  ChunkLoc cl;
-  if (!locate_chunk(p, gc, cl)) return;
-  const int hq = hv / (p.HV / p.HQK);
-
   const int tid = threadIdx.x;
   // wave index via readfirstlane: branches on it stay scalar (an MFMA under a
   // lane-predicated branch would still write every lane)
@@ -156,19 +159,24 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
   const int ln = tid & 63;
   const int r = ln & 15, g = ln >> 4;
   const int i = 16 * I + r;       // this lane's row in the chunk
-  const bool valid = i < cl.L;
-  const int64_t tok = (int64_t)cl.b * p.T + cl.row0 + i;
-  uint8_t* rec = p.recs + rec_index(hv, gc, p.max_chunks) * (int64_t)R::BYTES;
 
-  // ---- phase 1: loads (P-order key dims), gate cumsum, factors --------------------
-  // lane dims for step s, element e: d = 32s + pidx(g, e)
-  uint4 uqs[S], uks[S];   // q, k kept packed (bf16) until used
-  float gl[S][8];
-  float bt;
-  {
-    const uint16_t* qrow = p.q + (tok * p.HQK + hq) * K;
-    const uint16_t* krow = p.k + (tok * p.HQK + hq) * K;
-    const uint16_t* grow = p.g + (tok * p.HV + hv) * K;
+  // Persistent: the first round of items is blockIdx-based (XCD-remapped), later
+  // items are handed out by an atomic ticket counter, so workgroups that run faster
+  // take more items.  The q, k, g, beta of the next item are loaded into registers
+  // while the current one is computed.  lane dims for step s, element e:
+  // d = 32s + pidx(g, e)
+  __shared__ int s_next;
+  uint4 nq[S], nk[S], ng[S];
+  uint32_t nb = 0;   // raw bf16 bits: converting here would wait for the loads
+  auto fetch = [&](int it) {
+    ChunkLoc c;
+    const bool ok = it < n_items && locate_chunk(p, it / p.HV, c);
+    const int h = it % p.HV;
+    const bool valid = ok && i < c.L;
+    const int64_t tk = ok ? (int64_t)c.b * p.T + c.row0 + i : 0;
+    const uint16_t* qrow = p.q + (tk * p.HQK + h / (p.HV / p.HQK)) * K;
+    const uint16_t* krow = p.k + (tk * p.HQK + h / (p.HV / p.HQK)) * K;
+    const uint16_t* grow = p.g + (tk * p.HV + h) * K;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const int lo = 32 * s + 4 * g, hi = lo + 16;
@@ -181,13 +189,44 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
         uk = make_uint4(k0.x, k0.y, k1.x, k1.y);
         ug = make_uint4(g0.x, g0.y, g1.x, g1.y);
       }
-      uqs[s] = uq;
-      uks[s] = uk;
-      unpack8(ug, gl[s]);
+      nq[s] = uq;
+      nk[s] = uk;
+      ng[s] = ug;
     }
-    bt = valid ? bf2f(p.beta[tok * p.HV + hv]) : 0.f;
-    if (g == 0) sBeta[i] = bt;
+    nb = 0;
+    if (valid) nb = p.beta[tk * p.HV + h];
+  };
+  int item = xcd_remap(blockIdx.x, gridDim.x);
+  fetch(item);
+  if (tid == 0) s_next = (int)gridDim.x + atomicAdd(p.counter, 1);
+  __syncthreads();
+  while (item < n_items) {
+  const int next = s_next;   // written before the last barrier; rewritten only after B9
+  const int hv = item % p.HV;
+  const int64_t gc = item / p.HV;
+  ChunkLoc cl;
+  const bool live = locate_chunk(p, gc, cl);   // uniform over the workgroup
+  uint4 uqs[S], uks[S];   // q, k kept packed (bf16) until used
+  float gl[S][8];
+  float bt;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    uqs[s] = nq[s];
+    uks[s] = nk[s];
+    unpack8(ng[s], gl[s]);
   }
+  bt = bf2f((uint16_t)nb);
+  if (!live) {   // varlen capacity padding or rejected table: nothing to write
+    fetch(next);
+    __syncthreads();   // every thread has read s_next
+    if (tid == 0) s_next = (int)gridDim.x + atomicAdd(p.counter, 1);
+    __syncthreads();
+    item = next;
+    continue;
+  }
+  uint8_t* rec = p.recs + rec_index(hv, gc, p.max_chunks) * (int64_t)R::BYTES;
+  if (g == 0) sBeta[i] = bt;
+
   // in-block inclusive cumsum over the 16 rows (lanes r = 0..15 of a DPP row)
 #pragma unroll
   for (int s = 0; s < S; ++s)
@@ -205,34 +244,18 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
   //   rows 0..3  E_I = exp(mu_I)            mu_I = prefix_I + tot_I / 2
   //   rows 4..7  F_I = exp(Gam_last - mu_I)
   //   rows 8..13 c_IJ = exp(mu_I - mu_J), pair (I,J) -> 8 + I(I-1)/2 + J
-  for (int idx = tid; idx < 14 * K; idx += NTHREADS) {
-    const int row = idx / K, d = idx - row * K;
+  {
+    constexpr int STEP = NTHREADS / K;            // table rows per pass (2 or 4)
+    const int d = tid % K, r0 = tid / K;          // r0 is uniform over a wave (64 divides K)
     const float t0 = sTot[d], t1 = sTot[K + d], t2 = sTot[2 * K + d], t3 = sTot[3 * K + d];
     const float m0 = 0.5f * t0, m1 = t0 + 0.5f * t1, m2 = t0 + t1 + 0.5f * t2, m3 = t0 + t1 + t2 + 0.5f * t3;
     const float G = t0 + t1 + t2 + t3;
-    float a;
-    switch (row) {
-      case 0: a = m0; break;
-      case 1: a = m1; break;
-      case 2: a = m2; break;
-      case 3: a = m3; break;
-      case 4: a = G - m0; break;
-      case 5: a = G - m1; break;
-      case 6: a = G - m2; break;
-      case 7: a = G - m3; break;
-      case 8: a = m1 - m0; break;    // (1,0)
-      case 9: a = m2 - m0; break;    // (2,0)
-      case 10: a = m2 - m1; break;   // (2,1)
-      case 11: a = m3 - m0; break;   // (3,0)
-      case 12: a = m3 - m1; break;   // (3,1)
-      default: a = m3 - m2; break;   // (3,2)
-    }
-    sTab[idx] = __builtin_amdgcn_exp2f(LOG2E * a);
-  }
-  if (tid < K) {
-    const int d = tid;
-    const float G = sTot[d] + sTot[K + d] + sTot[2 * K + d] + sTot[3 * K + d];
-    reinterpret_cast<float*>(rec + R::ALPHA)[d] = __builtin_amdgcn_exp2f(LOG2E * G);
+    const float arg[14] = {m0, m1, m2, m3, G - m0, G - m1, G - m2, G - m3,
+                           m1 - m0, m2 - m0, m2 - m1, m3 - m0, m3 - m1, m3 - m2};
+#pragma unroll
+    for (int row = 0; row < 14; ++row)
+      if (row % STEP == r0) sTab[row * K + d] = __builtin_amdgcn_exp2f(LOG2E * arg[row]);
+    if (r0 == 0) reinterpret_cast<float*>(rec + R::ALPHA)[d] = __builtin_amdgcn_exp2f(LOG2E * G);
   }
   __syncthreads();  // B2: tables
 
@@ -284,8 +307,7 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
     KX[s] = as_frag(make_uint4(pk[0].x, pk[0].y, pk[1].x, pk[1].y));
     KYr[s] = as_frag(make_uint4(py[0].x, py[0].y, py[1].x, py[1].y));
     KD[s] = make_uint4(pd[0].x, pd[0].y, pd[1].x, pd[1].y);
-    *reinterpret_cast<uint4*>(rec + R::QG + ((I * S + s) * 64 + ln) * 16) =
-        make_uint4(pg[0].x, pg[0].y, pg[1].x, pg[1].y);
+    store_stream(rec + R::QG + ((I * S + s) * 64 + ln) * 16, make_uint4(pg[0].x, pg[0].y, pg[1].x, pg[1].y));
   }
   __syncthreads();  // B3: k*Y blocks, kg^T
 
@@ -296,7 +318,7 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
     const uint16_t* row = sKT + d * SM::TS;
     const uint2 lo = *reinterpret_cast<const uint2*>(row + tcol(32 * s2 + 4 * g, d));
     const uint2 hi = *reinterpret_cast<const uint2*>(row + tcol(32 * s2 + 16 + 4 * g, d));
-    *reinterpret_cast<uint4*>(rec + R::KGT + (f * 64 + ln) * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    store_stream(rec + R::KGT + (f * 64 + ln) * 16, make_uint4(lo.x, lo.y, hi.x, hi.y));
   }
   __syncthreads();  // B4: every read of kg^T is done
 #pragma unroll
@@ -352,34 +374,51 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
       }
     }
     if (s2 < tri_steps(I))
-      *reinterpret_cast<uint4*>(rec + R::AQK + (tri_frag(I, s2) * 64 + ln) * 16) = pack_pair(vq[0], vq[1]);
+      store_stream(rec + R::AQK + (tri_frag(I, s2) * 64 + ln) * 16, pack_pair(vq[0], vq[1]));
   }
   __syncthreads();  // B5: every read of k*Y is done (Akk reuses its space)
 #pragma unroll
   for (int J = 0; J < 4; ++J)
     *reinterpret_cast<float4*>(sAkk + i * SM::AS + 16 * J + 4 * g) = make_float4(vk[J][0], vk[J][1], vk[J][2], vk[J][3]);
   __syncthreads();  // B6: Akk and (k exp(Gam))^T complete
+  // the next item's inputs load during phases 3 and 4 (few registers live there)
+  fetch(next);
 
   // ---- phase 3: Tm = (I + Akk)^-1 ------------------------------------------------
-  // 3a: inverse of the unit lower diagonal block I, one column (r) per lane, by
-  //     forward substitution: x_i = -sum_{m<i} A[i][m] x_m for i > r, x_r = 1.
+  // 3a: inverse of the unit lower diagonal block I + N (N strictly lower, so
+  //     N^16 = 0): (I + N)^-1 = sum_k (-N)^k = (I - N)(I + N^2)(I + N^4)(I + N^8).
+  //     All operands stay in the 16x16 C layout.  With the contraction index of
+  //     step kb = 4g + kb in lane group g, the C layout of X^T is exactly the A
+  //     operand of X and the C layout of Y the B operand of Y, so a product needs
+  //     X^T and Y in C layout and returns X Y in C layout.  The powers of N
+  //     commute with the partial products, which are built as D <- D + N^(2^j) D.
   {
-    float x[16];
+    auto mm = [&](const f32x4& xt, const f32x4& y) {
+      f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int m = 0; m < 16; ++m) x[m] = (m == r) ? 1.f : 0.f;
+      for (int kb = 0; kb < 4; ++kb) c = mfma16x4f32(xt[kb], y[kb], c);
+      return c;
+    };
     const float* A = sAkk + (16 * I) * SM::AS + 16 * I;
+    f32x4 N, NT;   // lane: N[4g+e][r] and N[r][4g+e]
 #pragma unroll
-    for (int ii = 1; ii < 16; ++ii) {
-      float acc = 0.f;
-#pragma unroll
-      for (int m = 0; m < ii; ++m) acc += A[ii * SM::AS + m] * x[m];
-      if (ii > r) x[ii] = -acc;
+    for (int e = 0; e < 4; ++e) N[e] = A[(4 * g + e) * SM::AS + r];
+    {
+      const float4 t = *reinterpret_cast<const float4*>(A + r * SM::AS + 4 * g);
+      NT = f32x4{t.x, t.y, t.z, t.w};
     }
-    if (g == 0) {
-      float* Aw = sAkk + (16 * I) * SM::AS + 16 * I;
+    const f32x4 N2 = mm(NT, N), N2T = mm(N, NT);
+    const f32x4 N4 = mm(N2T, N2), N4T = mm(N2, N2T);
+    const f32x4 N8T = mm(N4, N4T);
+    f32x4 D;
 #pragma unroll
-      for (int ii = 0; ii < 16; ++ii) Aw[ii * SM::AS + r] = x[ii];
-    }
+    for (int e = 0; e < 4; ++e) D[e] = (4 * g + e == r ? 1.f : 0.f) - N[e];
+    D += mm(N2T, D);
+    D += mm(N4T, D);
+    D += mm(N8T, D);
+    float* Aw = sAkk + (16 * I) * SM::AS + 16 * I;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Aw[(4 * g + e) * SM::AS + r] = D[e];
   }
   __syncthreads();  // B7: diagonal blocks hold D_I
 
@@ -440,7 +479,7 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
                         t1.x * b1.x, t1.y * b1.y, t1.z * b1.z, t1.w * b1.w};
     const uint4 u = pack8(t);
     TB[s2] = as_frag(u);
-    *reinterpret_cast<uint4*>(rec + R::TMB + (tri_frag(I, s2) * 64 + ln) * 16) = u;
+    store_stream(rec + R::TMB + (tri_frag(I, s2) * 64 + ln) * 16, u);
   }
   // C[d][t] = sum_t' kd[t'][d] TmB[t][t'] = w[t][d]: lane holds w row 16I + r at
   // key dims 16md + 4g + rr, so tile pairs (md = 2s, 2s+1) form WN fragment (I, s).
@@ -460,7 +499,11 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
         acc[h] = mfma16x32(as_frag(make_uint4(lo.x, lo.y, hi.x, hi.y)), TB[s2], acc[h]);
       }
     }
-    *reinterpret_cast<uint4*>(rec + R::WN + ((I * S + s) * 64 + ln) * 16) = pack_pair(-acc[0], -acc[1]);
+    store_stream(rec + R::WN + ((I * S + s) * 64 + ln) * 16, pack_pair(-acc[0], -acc[1]));
+  }
+  if (tid == 0) s_next = (int)gridDim.x + atomicAdd(p.counter, 1);   // ticket for the item after next
+  __syncthreads();  // B10: phase-4 reads of Tm, beta and (k exp(Gam))^T are done; s_next visible
+  item = next;
   }
 }
 
@@ -534,10 +577,29 @@ hipError_t launch_chunk_table(const Params& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device id).
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+hipError_t launch_prep(const Params& p, hipStream_t s) {
+  hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(64), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_intra(const Params& p, hipStream_t s) {
   const int64_t items = p.max_chunks * p.HV;
   if (items == 0) return hipSuccess;
-  const int grid = padded8(items);
+  // persistent grid: KDA_INTRA_OCC resident workgroups per CU, each looping over items
+  const int grid = padded8(std::min<int64_t>(items, (int64_t)device_cus() * KDA_INTRA_OCC));
   if (p.K == 128) hipLaunchKernelGGL(intra_kernel<128>, dim3(grid), dim3(NTHREADS), 0, s, p, (int)items);
   else hipLaunchKernelGGL(intra_kernel<64>, dim3(grid), dim3(NTHREADS), 0, s, p, (int)items);
   return hipGetLastError();

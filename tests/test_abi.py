@@ -70,13 +70,16 @@ def ws(a):
 
 def test_workspace_bytes(lib):
     # fixed length: B * ceil(T/64) chunks per value head, one record per (chunk, head)
+    # plus a 256-byte header (work counter; varlen chunk table)
     st, n = ws(args(B=1, T=8192, HQK=32, HV=32))
-    assert st == 0 and n == 128 * 32 * 61952
+    assert st == 0 and n == 256 + 128 * 32 * 61952
     st, n = ws(args(B=2, T=200, HQK=1, HV=1, K=64, V=64, N=2))
-    assert st == 0 and n == 2 * 4 * 37120
-    # varlen: ceil(T/64) + N chunk capacity plus the 256-byte chunk table
+    assert st == 0 and n == 256 + 2 * 4 * 37120
+    # varlen: ceil(T/64) + N chunk capacity; the chunk table shares the header
     st, n = ws(args(B=1, T=1000, HQK=1, HV=2, N=5, cu_seqlens=1 << 20))
     assert st == 0 and n == 256 + (16 + 5) * 2 * 61952
+    st, n = ws(args(B=1, T=1000, HQK=1, HV=2, N=70, cu_seqlens=1 << 20))
+    assert st == 0 and n == 512 + (16 + 70) * 2 * 61952
     st, n = ws(args(T=0))
     assert st == 0 and n == 0
 
