@@ -163,38 +163,42 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
   // Persistent: the first round of items is blockIdx-based (XCD-remapped), later
   // items are handed out by an atomic ticket counter, so workgroups that run faster
   // take more items.  The q, k, g, beta of the next item are loaded into registers
-  // while the current one is computed.  lane dims for step s, element e:
+  // while the current one is computed (phases 2-3).  lane dims for step s, element e:
   // d = 32s + pidx(g, e)
   __shared__ int s_next;
   uint4 nq[S], nk[S], ng[S];
   uint32_t nb = 0;   // raw bf16 bits: converting here would wait for the loads
-  auto fetch = [&](int it) {
+  // one input of the next item: 0 = q, 1 = k, 2 = g and beta
+  auto fetch_part = [&](int it, int part) {
     ChunkLoc c;
     const bool ok = it < n_items && locate_chunk(p, it / p.HV, c);
     const int h = it % p.HV;
     const bool valid = ok && i < c.L;
     const int64_t tk = ok ? (int64_t)c.b * p.T + c.row0 + i : 0;
-    const uint16_t* qrow = p.q + (tk * p.HQK + h / (p.HV / p.HQK)) * K;
-    const uint16_t* krow = p.k + (tk * p.HQK + h / (p.HV / p.HQK)) * K;
-    const uint16_t* grow = p.g + (tk * p.HV + h) * K;
+    const uint16_t* row = part == 0 ? p.q + (tk * p.HQK + h / (p.HV / p.HQK)) * K
+                        : part == 1 ? p.k + (tk * p.HQK + h / (p.HV / p.HQK)) * K
+                                    : p.g + (tk * p.HV + h) * K;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const int lo = 32 * s + 4 * g, hi = lo + 16;
-      uint4 uq = make_uint4(0, 0, 0, 0), uk = uq, ug = uq;
+      uint4 u = make_uint4(0, 0, 0, 0);
       if (valid) {
-        const uint2 q0 = *reinterpret_cast<const uint2*>(qrow + lo), q1 = *reinterpret_cast<const uint2*>(qrow + hi);
-        const uint2 k0 = *reinterpret_cast<const uint2*>(krow + lo), k1 = *reinterpret_cast<const uint2*>(krow + hi);
-        const uint2 g0 = *reinterpret_cast<const uint2*>(grow + lo), g1 = *reinterpret_cast<const uint2*>(grow + hi);
-        uq = make_uint4(q0.x, q0.y, q1.x, q1.y);
-        uk = make_uint4(k0.x, k0.y, k1.x, k1.y);
-        ug = make_uint4(g0.x, g0.y, g1.x, g1.y);
+        const uint2 a0 = *reinterpret_cast<const uint2*>(row + lo), a1 = *reinterpret_cast<const uint2*>(row + hi);
+        u = make_uint4(a0.x, a0.y, a1.x, a1.y);
       }
-      nq[s] = uq;
-      nk[s] = uk;
-      ng[s] = ug;
+      if (part == 0) nq[s] = u;
+      else if (part == 1) nk[s] = u;
+      else ng[s] = u;
     }
-    nb = 0;
-    if (valid) nb = p.beta[tk * p.HV + h];
+    if (part == 2) {
+      nb = 0;
+      if (valid) nb = p.beta[tk * p.HV + h];
+    }
+  };
+  auto fetch = [&](int it) {
+    fetch_part(it, 0);
+    fetch_part(it, 1);
+    fetch_part(it, 2);
   };
   int item = xcd_remap(blockIdx.x, gridDim.x);
   fetch(item);
@@ -321,6 +325,10 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
     store_stream(rec + R::KGT + (f * 64 + ln) * 16, make_uint4(lo.x, lo.y, hi.x, hi.y));
   }
   __syncthreads();  // B4: every read of kg^T is done
+  // The next item's inputs load in three parts spread over phases 2-3 (g here, q
+  // after B6, k after B7): issued at once they waited about 6k cycles per item
+  // for queue space behind this item's record stores.
+  fetch_part(next, 2);   // g and beta of the next item
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const uint32_t wd[4] = {KD[s].x, KD[s].y, KD[s].z, KD[s].w};
@@ -381,8 +389,7 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
   for (int J = 0; J < 4; ++J)
     *reinterpret_cast<float4*>(sAkk + i * SM::AS + 16 * J + 4 * g) = make_float4(vk[J][0], vk[J][1], vk[J][2], vk[J][3]);
   __syncthreads();  // B6: Akk and (k exp(Gam))^T complete
-  // the next item's inputs load during phases 3 and 4 (few registers live there)
-  fetch(next);
+  fetch_part(next, 0);   // q of the next item
 
   // ---- phase 3: Tm = (I + Akk)^-1 ------------------------------------------------
   // 3a: inverse of the unit lower diagonal block I + N (N strictly lower, so
@@ -421,6 +428,7 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
     for (int e = 0; e < 4; ++e) Aw[(4 * g + e) * SM::AS + r] = D[e];
   }
   __syncthreads();  // B7: diagonal blocks hold D_I
+  fetch_part(next, 1);   // k of the next item
 
   // 3b: block column J = I below the diagonal:
   //     Inv_MJ = -D_M sum_{J<=P<M} A_MP Inv_PJ   (Inv_JJ = D_J),
