@@ -93,6 +93,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true", help="skip timing the forward's options")
     ap.add_argument("--cold", type=int, default=20, help="extra cold-cache steps (flush between)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -165,6 +166,33 @@ def main():
         cold_ms = float(np.median(cold))
         del flush
 
+    # the forward's options, same workload (informational; not the headline)
+    variants_ms = None
+    if not args.no_variants:
+        from gated_delta_rule_chunked_amd import KDA_FLAG_BETA_LOGITS, KDA_FLAG_STATE_BF16, num_chunks
+        variants_ms = {}
+        ht_bf = torch.empty((N, HV, K, V), dtype=torch.bfloat16, device=dev)
+        hc = torch.empty((num_chunks(T, None, B), HV, K, V), dtype=torch.float32, device=dev)
+        for name, kw in (("beta_logits", dict(flags=KDA_FLAG_BETA_LOGITS, ht=ht)),
+                         ("bf16_state", dict(flags=KDA_FLAG_STATE_BF16, ht=ht_bf)),
+                         ("chunk_states_fp32", dict(flags=0, ht=ht, hc=hc))):
+            ht_v = kw.pop("ht")
+            av = make_args(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], None, None, o, ht_v,
+                           stream=stream.cuda_stream, **kw)
+            av.workspace, av.workspace_bytes = ws.data_ptr(), ws.numel()
+            for _ in range(2):
+                kda_fwd_intra(av)
+                kda_fwd_inter(av)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(10):
+                kda_fwd_intra(av)
+                kda_fwd_inter(av)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            variants_ms[name] = e0.elapsed_time(e1) / 10
+        del hc, ht_bf
+
     tokens = B * T
     value = tokens / (ms_per_step * 1e-3)
     ab_intra, ab_inter = algorithmic_bytes(d)
@@ -197,6 +225,7 @@ def main():
                           "hbm_frac": path_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
                           "mfma_frac": flops / (ms_per_step * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12)},
         "cold_cache_ms_per_step": cold_ms,
+        "options_ms_per_step": variants_ms,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(d)

@@ -10,6 +10,14 @@
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
+static_assert(offsetof(kda_fwd_args, scale) == 40 && offsetof(kda_fwd_args, B) == 64 &&
+                  offsetof(kda_fwd_args, o) == 96 && offsetof(kda_fwd_args, stream) == 128 &&
+                  offsetof(kda_fwd_args, flags) == 136 && offsetof(kda_fwd_args, hc) == 144 &&
+                  sizeof(kda_fwd_args) == 152,
+              "argument struct layout (mirrored by the Python binding)");
+static_assert(kda::FLAG_BETA_LOGITS == KDA_FLAG_BETA_LOGITS && kda::FLAG_STATE_BF16 == KDA_FLAG_STATE_BF16,
+              "flag bits match the public header");
+
 namespace {
 
 thread_local char g_hip_msg[256] = "no HIP error recorded";
@@ -63,7 +71,8 @@ int check_call(const kda_fwd_args* a, int need, kda::Params* p) {
     if (!aligned(a->v, 16) || !aligned(a->o, 8) || !aligned(a->h0, 16) || !aligned(a->ht, 16))
       return KDA_ERR_INVALID_ARG;
   }
-  if (!aligned(a->cu_seqlens, 8)) return KDA_ERR_INVALID_ARG;
+  if (!aligned(a->cu_seqlens, 8) || !aligned(a->hc, 16)) return KDA_ERR_INVALID_ARG;
+  if (a->flags & ~(uint32_t)(KDA_FLAG_BETA_LOGITS | KDA_FLAG_STATE_BF16)) return KDA_ERR_INVALID_ARG;
   if (L.total_bytes > 0) {
     if (!a->workspace || !aligned(a->workspace, 256)) return KDA_ERR_WORKSPACE;
     if (a->workspace_bytes < (size_t)L.total_bytes) return KDA_ERR_WORKSPACE;
@@ -78,6 +87,8 @@ int check_call(const kda_fwd_args* a, int need, kda::Params* p) {
   p->cu = a->cu_seqlens;
   p->o = (uint16_t*)a->o;
   p->ht = a->ht;
+  p->hc = a->hc;
+  p->flags = a->flags;
   p->counter = (int32_t*)a->workspace;
   p->table = a->cu_seqlens ? (int32_t*)((uint8_t*)a->workspace + 16) : nullptr;
   p->recs = (uint8_t*)a->workspace + L.table_bytes;

@@ -82,6 +82,15 @@ __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// States (h0, ht, hc) are fp32, or bf16 with FLAG_STATE_BF16.
+__device__ __forceinline__ float load_state(const Params& p, const void* base, int64_t idx) {
+  return (p.flags & FLAG_STATE_BF16) ? bf2f(static_cast<const uint16_t*>(base)[idx]) : static_cast<const float*>(base)[idx];
+}
+__device__ __forceinline__ void store_state(const Params& p, void* base, int64_t idx, float x) {
+  if (p.flags & FLAG_STATE_BF16) static_cast<uint16_t*>(base)[idx] = f2bf(x);
+  else static_cast<float*>(base)[idx] = x;
+}
+
 __device__ __forceinline__ uint2 pack4(const f32x4& a) {
   return make_uint2(pack2(a[0], a[1]), pack2(a[2], a[3]));
 }
@@ -118,7 +127,7 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void inter_kernel(Params p, int n
       const float qnan = __builtin_nanf("");
       if (p.ht)
         for (int idx = tid; idx < K * BV; idx += INTER_THREADS)
-          p.ht[(((int64_t)n * p.HV + hv) * K + idx / BV) * p.V + vt * BV + idx % BV] = qnan;
+          store_state(p, p.ht, (((int64_t)n * p.HV + hv) * K + idx / BV) * p.V + vt * BV + idx % BV, qnan);
       const int64_t total = (int64_t)p.B * p.T * p.HV * p.V;
       for (int64_t idx = (int64_t)item * INTER_THREADS + tid; idx < total; idx += (int64_t)n_items * INTER_THREADS)
         p.o[idx] = 0x7fc0;
@@ -140,11 +149,32 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void inter_kernel(Params p, int n
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int d = 16 * md + 4 * g + rr;
-        h[md][rr] = p.h0 ? p.h0[(((int64_t)n * p.HV + hv) * K + d) * p.V + vt * BV + r] : 0.f;
+        h[md][rr] = p.h0 ? load_state(p, p.h0, (((int64_t)n * p.HV + hv) * K + d) * p.V + vt * BV + r) : 0.f;
       }
     barrier_lds();  // S0
     for (int ph = 0; ph < nphase; ++ph) {
       if (ph < nc) {
+        if (p.hc) {   // the state before this chunk; uniform branches, before the operand batches
+          // The row stride is re-made opaque every chunk, so the 32 row offsets stay
+          // transient scalars instead of being hoisted out of the loop as live
+          // 64-bit addresses (which spilled the whole kernel).
+          int sv = p.V;
+          asm volatile("" : "+s"(sv));
+          const int64_t base = (((sq.cbase + ph) * p.HV + hv) * K + 4 * g) * (int64_t)sv + vt * BV + r;
+          if (p.flags & FLAG_STATE_BF16) {
+            uint16_t* dst = static_cast<uint16_t*>(p.hc) + base;
+#pragma unroll
+            for (int md = 0; md < ND; ++md)
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) dst[(int64_t)(16 * md + rr) * sv] = f2bf(h[md][rr]);
+          } else {
+            float* dst = static_cast<float*>(p.hc) + base;
+#pragma unroll
+            for (int md = 0; md < ND; ++md)
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) dst[(int64_t)(16 * md + rr) * sv] = h[md][rr];
+          }
+        }
         const uint8_t* st = smem + SM::ST + (ph & 1) * SM::STAGE;
         const uint16_t* vrow = reinterpret_cast<const uint16_t*>(smem + SM::VT) + (ph & 1) * BV * SM::VS + r * SM::VS;
         // batch 1: v^T, TmB, decay, -w (in the order they are consumed)
@@ -215,7 +245,7 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void inter_kernel(Params p, int n
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int d = 16 * md + 4 * g + rr;
-          p.ht[(((int64_t)n * p.HV + hv) * K + d) * p.V + vt * BV + r] = h[md][rr];
+          store_state(p, p.ht, (((int64_t)n * p.HV + hv) * K + d) * p.V + vt * BV + r, h[md][rr]);
         }
     }
   } else if (wave <= 4) {

@@ -7,20 +7,26 @@
 
 namespace kda {
 
+// kda_fwd_args.flags bits (same values as KDA_FLAG_* in include/kda.h)
+constexpr uint32_t FLAG_BETA_LOGITS = 1u;
+constexpr uint32_t FLAG_STATE_BF16 = 2u;
+
 struct Params {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* g;
   const uint16_t* beta;
-  const float* h0;
+  const void* h0;       // fp32, or bf16 with KDA_FLAG_STATE_BF16
   const int64_t* cu;     // varlen cu_seqlens or nullptr
   uint16_t* o;
-  float* ht;
+  void* ht;             // state dtype
   int32_t* table;        // varlen: chunk_base[N+1], then error flag at [N+1]
   int32_t* counter;      // work counter of the intra stage (zeroed by the prep kernel)
+  void* hc;              // per-chunk states (state dtype) or nullptr
   uint8_t* recs;         // workspace records
   float scale;
+  uint32_t flags;        // KDA_FLAG_* bits
   int B, T, HQK, HV, K, V, N;
   int NT;                // fixed length: chunks per sequence
   int64_t max_chunks;    // workspace capacity in chunks (per value head)

@@ -191,7 +191,8 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
       else ng[s] = u;
     }
     if (part == 2) {
-      nb = 0;
+      // rows past the chunk get beta = 0: the bf16 bits of 0, or of -inf as a logit
+      nb = (p.flags & FLAG_BETA_LOGITS) ? 0xff80u : 0u;
       if (valid) nb = p.beta[tk * p.HV + h];
     }
   };
@@ -220,6 +221,8 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
     unpack8(ng[s], gl[s]);
   }
   bt = bf2f((uint16_t)nb);
+  if (p.flags & FLAG_BETA_LOGITS)   // FlashKDA's fused sigmoid: 1 / (1 + e^-x), exact 0 and 1 at -inf, +inf
+    bt = 1.f / (1.f + __builtin_amdgcn_exp2f(-LOG2E * bt));
   if (!live) {   // varlen capacity padding or rejected table: nothing to write
     fetch(next);
     __syncthreads();   // every thread has read s_next

@@ -20,6 +20,8 @@ KDA_ERR_UNSUPPORTED = -2
 KDA_ERR_WORKSPACE = -3
 KDA_ERR_HIP = -4
 KDA_CHUNK = 64
+KDA_FLAG_BETA_LOGITS = 1
+KDA_FLAG_STATE_BF16 = 2
 
 EXPORTED = ("kda_fwd_workspace_bytes", "kda_fwd", "kda_fwd_intra", "kda_fwd_inter",
             "kda_debug_unpack", "kda_strerror")
@@ -35,6 +37,7 @@ class KdaFwdArgs(ctypes.Structure):
         ("o", c_void_p), ("ht", c_void_p),
         ("workspace", c_void_p), ("workspace_bytes", c_size_t),
         ("stream", c_void_p),
+        ("flags", ctypes.c_uint32), ("hc", c_void_p),
     ]
 
 
@@ -78,21 +81,24 @@ def _ptr(t):
 
 
 def make_args(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, o=None, ht=None,
-              workspace=None, stream=None) -> KdaFwdArgs:
+              workspace=None, stream=None, flags=0, hc=None) -> KdaFwdArgs:
     """Fill ``kda_fwd_args`` from torch tensors (shapes as in the header).
 
     q, k: [B, T, HQK, K] bf16; v: [B, T, HV, V] bf16; g: [B, T, HV, K] bf16;
-    beta: [B, T, HV] bf16; h0: [N, HV, K, V] fp32 or None; cu_seqlens: int64 [N+1]
-    on the device or None.  Only pointers and sizes are read here.
+    beta: [B, T, HV] bf16; h0: [N, HV, K, V] or None; cu_seqlens: int64 [N+1]
+    on the device or None; hc: [C, HV, K, V] or None.  States (h0, ht, hc) are
+    fp32, or bf16 with KDA_FLAG_STATE_BF16 in ``flags``.  Only pointers and sizes
+    are read here.
     """
     import torch
     B, T, HQK, K = q.shape
     HV, V = v.shape[2], v.shape[3]
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    sdt = torch.bfloat16 if flags & KDA_FLAG_STATE_BF16 else torch.float32
     for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16), ("v", v, torch.bfloat16),
                         ("g", g, torch.bfloat16), ("beta", beta, torch.bfloat16),
-                        ("h0", h0, torch.float32), ("cu_seqlens", cu_seqlens, torch.int64),
-                        ("o", o, torch.bfloat16), ("ht", ht, torch.float32)):
+                        ("h0", h0, sdt), ("cu_seqlens", cu_seqlens, torch.int64),
+                        ("o", o, torch.bfloat16), ("ht", ht, sdt), ("hc", hc, sdt)):
         if t is not None:
             if t.dtype != dt:
                 raise TypeError(f"{name} must be {dt}, got {t.dtype}")
@@ -109,6 +115,8 @@ def make_args(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, o=None, ht
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a.stream = stream
+    a.flags = int(flags)
+    a.hc = _ptr(hc)
     return a
 
 
@@ -144,11 +152,24 @@ def alloc_workspace(args: KdaFwdArgs, device):
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
-def kda_fwd(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, output_final_state=True,
-            o=None, workspace=None):
-    """Chunked KDA forward on the current stream; returns (o, ht or None).
+def num_chunks(T, cu_seqlens=None, B=1):
+    """Chunks over all sequences: B * ceil(T/64), or sum_n ceil(len_n/64) for varlen
+    (cu_seqlens is read on the host; a device tensor is copied)."""
+    if cu_seqlens is None:
+        return B * ((T + KDA_CHUNK - 1) // KDA_CHUNK)
+    cu = [int(x) for x in cu_seqlens.detach().cpu().tolist()]
+    return sum((cu[i + 1] - cu[i] + KDA_CHUNK - 1) // KDA_CHUNK for i in range(len(cu) - 1))
 
-    Allocates o, ht and the workspace with torch unless given.
+
+def kda_fwd(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, output_final_state=True,
+            o=None, workspace=None, beta_logits=False, state_dtype=None, output_chunk_states=False):
+    """Chunked KDA forward on the current stream.
+
+    Returns (o, ht or None), or (o, ht or None, hc) with ``output_chunk_states``:
+    hc [C, HV, K, V] is the state before each chunk (see ``num_chunks``).
+    ``beta_logits``: beta holds logits and the kernel applies the sigmoid.
+    ``state_dtype``: torch.float32 (default) or torch.bfloat16 for h0, ht and hc.
+    Allocates o, ht, hc and the workspace with torch unless given.
     """
     import torch
     if not q.is_cuda:
@@ -157,16 +178,23 @@ def kda_fwd(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, output_final
     B, T, _, K = q.shape
     HV, V = v.shape[2], v.shape[3]
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    sdt = torch.float32 if state_dtype is None else state_dtype
+    if sdt not in (torch.float32, torch.bfloat16):
+        raise TypeError("state_dtype must be torch.float32 or torch.bfloat16")
+    flags = (KDA_FLAG_BETA_LOGITS if beta_logits else 0) | (KDA_FLAG_STATE_BF16 if sdt == torch.bfloat16 else 0)
     if o is None:
         o = torch.empty((B, T, HV, V), dtype=torch.bfloat16, device=q.device)
-    ht = torch.empty((N, HV, K, V), dtype=torch.float32, device=q.device) if output_final_state else None
-    args = make_args(q, k, v, g, beta, scale, h0, cu_seqlens, o, ht)
+    ht = torch.empty((N, HV, K, V), dtype=sdt, device=q.device) if output_final_state else None
+    hc = None
+    if output_chunk_states:
+        hc = torch.empty((num_chunks(T, cu_seqlens, B), HV, K, V), dtype=sdt, device=q.device)
+    args = make_args(q, k, v, g, beta, scale, h0, cu_seqlens, o, ht, flags=flags, hc=hc)
     if workspace is None:
         workspace = alloc_workspace(args, q.device)
     args.workspace = workspace.data_ptr()
     args.workspace_bytes = workspace.numel() * workspace.element_size()
     kda_fwd_raw(args)
-    return o, ht
+    return (o, ht, hc) if output_chunk_states else (o, ht)
 
 
 def kda_debug_unpack(args: KdaFwdArgs, qg=None, w=None, kg=None, aqk=None, tmb=None, alpha=None):

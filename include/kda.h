@@ -48,14 +48,20 @@ extern "C" {
 /* Chunk length of the chunked form (tokens per chunk). */
 #define KDA_CHUNK 64
 
+/* Option bits of kda_fwd_args.flags (FlashKDA's input and state variants,
+ * "KDA源码剖析之FlashKDA（下）", parameter list of the forward entry point). */
+#define KDA_FLAG_BETA_LOGITS  1u  /* beta holds raw logits; the kernel applies the sigmoid */
+#define KDA_FLAG_STATE_BF16   2u  /* h0, ht and hc are bf16 instead of fp32                */
+
 typedef struct kda_fwd_args {
   /* Inputs (device, bf16 unless stated).
    *   q, k : [B, T, HQK, K]  keys/queries, expected L2-normalised over K by the caller
    *   v    : [B, T, HV,  V]
    *   g    : [B, T, HV,  K]  natural-log per-dimension decay, g <= 0
-   *   beta : [B, T, HV]      write strength in [0, 1] (already through a sigmoid)
-   *   h0   : fp32 [N, HV, K, V] initial state per sequence and value head, or NULL
-   *          for a zero initial state.
+   *   beta : [B, T, HV]      write strength in [0, 1] (already through a sigmoid),
+   *          or its logit with KDA_FLAG_BETA_LOGITS
+   *   h0   : [N, HV, K, V] initial state per sequence and value head, fp32 (bf16
+   *          with KDA_FLAG_STATE_BF16), or NULL for a zero initial state.
    *   cu_seqlens : int64 [N + 1] on the device, or NULL.  NULL = fixed length:
    *          N = B sequences of T tokens.  Non-NULL = varlen: B must be 1, the N
    *          sequences are rows [cu[n], cu[n+1]) of the packed row, cu[0] = 0,
@@ -69,22 +75,32 @@ typedef struct kda_fwd_args {
   const void* g;
   const void* beta;
   float scale;                 /* usually K^-0.5                                      */
-  const float* h0;
+  const void* h0;
   const int64_t* cu_seqlens;
   int32_t B, T, HQK, HV, K, V; /* K in {64, 128}; V a positive multiple of 16         */
   int32_t N;                   /* number of sequences: == B (fixed) or len(cu) - 1    */
   /* Outputs (device, caller-allocated).
    *   o  : bf16 [B, T, HV, V]   every row of every sequence is written
-   *   ht : fp32 [N, HV, K, V]   final state per sequence, or NULL to skip it
+   *   ht : [N, HV, K, V]   final state per sequence (state dtype), or NULL to skip
    * Alignment (else KDA_ERR_INVALID_ARG): q, k, v, g, h0, ht 16 bytes; o and
    * cu_seqlens 8 bytes; beta 2 bytes.  All tensors are dense, row-major.       */
   void* o;
-  float* ht;
+  void* ht;
   /* Scratch (device, caller-allocated, 256-byte aligned, size from
    * kda_fwd_workspace_bytes).  Contents on entry do not matter. */
   void* workspace;
   size_t workspace_bytes;
   void* stream;                /* hipStream_t */
+  /* Options; all-zero keeps the behaviour described above. */
+  uint32_t flags;              /* KDA_FLAG_* bits; unknown bits are rejected          */
+  /* Per-chunk states (kda_fwd / kda_fwd_inter), or NULL to skip them:
+   *   hc : [C, HV, K, V] in the state dtype, the state *before* each chunk, chunks
+   *        numbered sequence by sequence (sequence n's chunk j is chunk
+   *        sum_{m<n} ceil(len_m / 64) + j; fixed length: n * ceil(T/64) + j),
+   *        C = that total.  Alignment 16 bytes (fp32) or 8 bytes (bf16).
+   * The chunked backward pass needs these (kernel-fun fwd_state module docstring,
+   * which keeps h per chunk for the backward). */
+  void* hc;
 } kda_fwd_args;
 
 /* Workspace size for these arguments (host only, launches nothing).  Only the

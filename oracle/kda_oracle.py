@@ -175,7 +175,9 @@ def chunked(q, k, v, g, beta, scale, h0=None, cu_seqlens=None, chunk: int = 64,
         o  = scale * qg h + Aqk v'
         h  = diag(exp(Gam_last)) h + kg^T v'
     With ``return_intermediates`` also returns a list of per-chunk dicts
-    (keys of ``_chunk_intermediates`` plus seq, row0, rows).
+    (keys of ``_chunk_intermediates`` plus seq, row0, rows, vp and h, the state
+    before the chunk [HV, K, V] -- the per-chunk states that the chunked backward
+    pass keeps).
     """
     q, k, v, g, beta = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g, beta))
     B, T, HQK, K = q.shape
@@ -192,12 +194,13 @@ def chunked(q, k, v, g, beta, scale, h0=None, cu_seqlens=None, chunk: int = 64,
             qc = q[b, r0:r1][:, hq]
             kc = k[b, r0:r1][:, hq]
             ci = _chunk_intermediates(qc, kc, v[b, r0:r1], g[b, r0:r1], beta[b, r0:r1], scale)
+            h_in = h
             vp = ci["u"] - np.einsum("ihd,hdv->ihv", ci["w"], h)
             o[b, r0:r1] = (scale * np.einsum("ihd,hdv->ihv", ci["qg"], h)
                            + np.einsum("hij,jhv->ihv", ci["Aqk"], vp))
             h = np.exp(ci["gd"])[:, :, None] * h + np.einsum("jhd,jhv->hdv", ci["kg"], vp)
             if return_intermediates:
-                ci.update(seq=n, row0=r0, rows=r1 - r0, vp=vp)
+                ci.update(seq=n, row0=r0, rows=r1 - r0, vp=vp, h=h_in)
                 inter.append(ci)
         ht[n] = h
     if return_intermediates:

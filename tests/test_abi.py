@@ -46,7 +46,8 @@ def test_struct_layout_matches_header():
     a = K.KdaFwdArgs
     assert a.scale.offset == 40 and a.h0.offset == 48 and a.cu_seqlens.offset == 56
     assert a.B.offset == 64 and a.N.offset == 88 and a.o.offset == 96
-    assert a.workspace_bytes.offset == 120 and a.stream.offset == 128 and ctypes.sizeof(a) == 136
+    assert a.workspace_bytes.offset == 120 and a.stream.offset == 128
+    assert a.flags.offset == 136 and a.hc.offset == 144 and ctypes.sizeof(a) == 152
 
 
 def args(**over):
@@ -105,6 +106,8 @@ INTER = ("kda_fwd", "kda_fwd_inter")     # entry points that read v, o, h0, ht
     (dict(o=0), K.KDA_ERR_INVALID_ARG, INTER),
     (dict(o=(1 << 20) + 4), K.KDA_ERR_INVALID_ARG, INTER),   # o needs 8 bytes
     (dict(h0=(1 << 20) + 4), K.KDA_ERR_INVALID_ARG, INTER),
+    (dict(flags=4), K.KDA_ERR_INVALID_ARG, ALL),              # unknown option bit
+    (dict(hc=(1 << 20) + 8), K.KDA_ERR_INVALID_ARG, ALL),     # misaligned per-chunk states
     (dict(workspace=0), K.KDA_ERR_WORKSPACE, ALL),
     (dict(workspace_bytes=1000), K.KDA_ERR_WORKSPACE, ALL),
     (dict(workspace=(1 << 20) + 128, workspace_bytes=1 << 40), K.KDA_ERR_WORKSPACE, ALL),

@@ -284,6 +284,24 @@ def test_chunked_matches_recurrent_varlen_gva(C):
     assert nerr(o2, o1) < 1e-10 and nerr(h2, h1) < 1e-10
 
 
+@pytest.mark.parametrize("C", [16, 64])
+def test_chunk_start_states_match_recurrent_states(C):
+    """The per-chunk states of the chunked form (the state before each chunk) are
+    the token recurrence's state after the chunk's previous token, or h0 at each
+    sequence start (varlen with empty and one-token sequences, GVA)."""
+    d, a = small(seed=23, K=16, V=8, HV=4, HQK=2, lengths=[70, 0, 129, 1, 64])
+    _, _, states = recurrent(**a, scale=d["scale"], h0=d["h0"], cu_seqlens=d["cu_seqlens"], return_states=True)
+    _, _, inter = chunked(**a, scale=d["scale"], h0=d["h0"], cu_seqlens=d["cu_seqlens"], chunk=C,
+                          return_intermediates=True)
+    cu = [int(x) for x in d["cu_seqlens"]]
+    n_chunks = sum(-(-(cu[i + 1] - cu[i]) // C) for i in range(len(cu) - 1))
+    assert len(inter) == n_chunks
+    for ci in inter:
+        n, r0 = ci["seq"], ci["row0"]
+        ref = d["h0"][n] if r0 == cu[n] else states[0, r0 - 1]
+        assert nerr(ci["h"], ref) < 1e-12, (n, r0)
+
+
 def test_chunk_intermediates_definitions():
     """The intra-stage pieces satisfy their defining relations: Tm (I + Akk) = I,
     Aqk is lower triangular with scale * q_i . k_i on the diagonal, and the
