@@ -3,4 +3,6 @@
 Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline leg
 may import this package.  The product path never does.
 """
-from .kda_oracle import recurrent, chunked, chunk_table, chunk_lengths, sequences  # noqa: F401
+from .kda_oracle import (  # noqa: F401
+    backward_states, bwd_dhu, chunk_lengths, chunk_table, chunked, recurrent, sequences, stage_inputs,
+)

@@ -206,3 +206,77 @@ def chunked(q, k, v, g, beta, scale, h0=None, cu_seqlens=None, chunk: int = 64,
     if return_intermediates:
         return o, ht, inter
     return o, ht
+
+
+def bwd_dhu(qg, kg, w, gcum, do, dv_in, scale, dht=None, cu_seqlens=None, chunk: int = 64):
+    """Reverse state scan of the chunked backward pass (the stage the kernel-fun page
+    "kernel_fun/kda/_kernels/bwd_dhu.py" documents in its module docstring), on
+    plain tensors.
+
+    qg, kg, w: [B, T, HV, K] (qg without scale, as in ``chunked``); gcum: [B, T, HV, K]
+    chunk-local inclusive cumsum of the natural-log gate (the chunk's decay is
+    exp(gcum) at its last row); do, dv_in: [B, T, HV, V]; dht: [N, HV, K, V] or None.
+    Per sequence and value head, dh = dht (or 0), chunks newest first:
+        dhc[c] = dh                               (gradient of the state after chunk c)
+        dv2    = kg dh + dv_in                    [L, V]
+        dh     = diag(exp(gcum_last)) dh + scale qg^T do - w^T dv2
+    and dh0 = dh after the first chunk.  Returns dv2 [B, T, HV, V], dhc [C, HV, K, V]
+    with chunks numbered sequence by sequence (as ``chunked``'s intermediates), and
+    dh0 [N, HV, K, V].
+    """
+    qg, kg, w, gcum, do, dv_in = (np.asarray(x, dtype=np.float64) for x in (qg, kg, w, gcum, do, dv_in))
+    B, T, HV, K = qg.shape
+    V = do.shape[3]
+    seqs = sequences(B, T, cu_seqlens)
+    dv2 = np.zeros((B, T, HV, V))
+    dh0 = np.zeros((len(seqs), HV, K, V))
+    dhc = []
+    for n, (b, bos, eos) in enumerate(seqs):
+        dh = np.zeros((HV, K, V)) if dht is None else np.array(dht[n], dtype=np.float64)
+        starts = list(range(bos, eos, chunk))
+        seq_dhc = [None] * len(starts)
+        for ci in range(len(starts) - 1, -1, -1):
+            r0 = starts[ci]
+            r1 = min(eos, r0 + chunk)
+            seq_dhc[ci] = dh
+            dv = np.einsum("jhd,hdv->jhv", kg[b, r0:r1], dh) + dv_in[b, r0:r1]
+            dv2[b, r0:r1] = dv
+            dh = (np.exp(gcum[b, r1 - 1])[:, :, None] * dh
+                  + scale * np.einsum("ihd,ihv->hdv", qg[b, r0:r1], do[b, r0:r1])
+                  - np.einsum("ihd,ihv->hdv", w[b, r0:r1], dv))
+        dhc.extend(seq_dhc)
+        dh0[n] = dh
+    dhc = np.stack(dhc) if dhc else np.zeros((0, HV, K, V))
+    return dv2, dhc, dh0
+
+
+def stage_inputs(q, k, v, g, beta, scale, do, cu_seqlens=None, chunk: int = 64):
+    """The forward's per-chunk operands laid out as the backward scan's plain
+    tensors: qg, kg, w, gcum [B, T, HV, K] and the local gradient dv_in = Aqk^T do
+    [B, T, HV, V] (the part of dL/dv' that does not pass through the state)."""
+    q, k, v, g, beta, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g, beta, do))
+    B, T, HQK, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    hq = _qk_head_map(HQK, HV)
+    out = {n: np.zeros((B, T, HV, K)) for n in ("qg", "kg", "w", "gcum")}
+    out["dv_in"] = np.zeros((B, T, HV, V))
+    for b, bos, eos in sequences(B, T, cu_seqlens):
+        for r0 in range(bos, eos, chunk):
+            r1 = min(eos, r0 + chunk)
+            ci = _chunk_intermediates(q[b, r0:r1][:, hq], k[b, r0:r1][:, hq], v[b, r0:r1],
+                                      g[b, r0:r1], beta[b, r0:r1], scale)
+            out["qg"][b, r0:r1] = ci["qg"]
+            out["kg"][b, r0:r1] = ci["kg"]
+            out["w"][b, r0:r1] = ci["w"]
+            out["gcum"][b, r0:r1] = ci["G"]
+            out["dv_in"][b, r0:r1] = np.einsum("hij,ihv->jhv", ci["Aqk"], do[b, r0:r1])
+    return out
+
+
+def backward_states(q, k, v, g, beta, scale, do, dht=None, cu_seqlens=None, chunk: int = 64):
+    """The state part of the chunked backward for the loss <do, o> + <dht, ht>:
+    dv2 = dL/dv' per token, dhc (gradient of the state after each chunk) and
+    dh0 = dL/dh0, via ``stage_inputs`` then ``bwd_dhu``."""
+    si = stage_inputs(q, k, v, g, beta, scale, do, cu_seqlens, chunk)
+    return bwd_dhu(si["qg"], si["kg"], si["w"], si["gcum"], do, si["dv_in"], scale, dht=dht,
+                   cu_seqlens=cu_seqlens, chunk=chunk)
