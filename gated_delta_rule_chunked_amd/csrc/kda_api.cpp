@@ -15,7 +15,12 @@ static_assert(offsetof(kda_fwd_args, scale) == 40 && offsetof(kda_fwd_args, B) =
                   offsetof(kda_fwd_args, flags) == 136 && offsetof(kda_fwd_args, hc) == 144 &&
                   sizeof(kda_fwd_args) == 152,
               "argument struct layout (mirrored by the Python binding)");
-static_assert(kda::FLAG_BETA_LOGITS == KDA_FLAG_BETA_LOGITS && kda::FLAG_STATE_BF16 == KDA_FLAG_STATE_BF16,
+static_assert(offsetof(kda_bwd_dhu_args, scale) == 56 && offsetof(kda_bwd_dhu_args, B) == 72 &&
+                  offsetof(kda_bwd_dhu_args, dv2) == 96 && offsetof(kda_bwd_dhu_args, stream) == 136 &&
+                  offsetof(kda_bwd_dhu_args, flags) == 144 && sizeof(kda_bwd_dhu_args) == 152,
+              "backward argument struct layout (mirrored by the Python binding)");
+static_assert(kda::FLAG_BETA_LOGITS == KDA_FLAG_BETA_LOGITS && kda::FLAG_STATE_BF16 == KDA_FLAG_STATE_BF16 &&
+                  kda::FLAG_CKPT_BF16 == KDA_FLAG_CKPT_BF16,
               "flag bits match the public header");
 
 namespace {
@@ -106,9 +111,30 @@ int hip_status(hipError_t e) {
   return KDA_ERR_HIP;
 }
 
+// Shape checks of the backward scan; the workspace holds only the varlen chunk table.
+int check_bwd_shapes(const kda_bwd_dhu_args* a, int64_t* ws_bytes) {
+  if (!a) return KDA_ERR_INVALID_ARG;
+  if (a->K != 64 && a->K != 128) return KDA_ERR_UNSUPPORTED;
+  if (a->V <= 0 || a->V % kda::BV != 0) return KDA_ERR_UNSUPPORTED;
+  if (a->B < 1 || a->T < 0 || a->HV < 1 || a->N < 1) return KDA_ERR_INVALID_ARG;
+  if (a->cu_seqlens) {
+    if (a->B != 1) return KDA_ERR_INVALID_ARG;
+  } else if (a->N != a->B) {
+    return KDA_ERR_INVALID_ARG;
+  }
+  if ((int64_t)a->B * a->T > ((int64_t)1 << 40)) return KDA_ERR_INVALID_ARG;
+  const int64_t nt = ((int64_t)a->T + kda::BT - 1) / kda::BT;
+  const int64_t max_chunks = a->cu_seqlens ? nt + a->N : (int64_t)a->B * nt;
+  if (max_chunks * a->HV >= ((int64_t)1 << 31) - 8) return KDA_ERR_INVALID_ARG;
+  if ((int64_t)a->N * a->HV * (a->V / kda::BV) >= ((int64_t)1 << 31) - 8) return KDA_ERR_INVALID_ARG;
+  if (a->N >= (1 << 30)) return KDA_ERR_INVALID_ARG;
+  *ws_bytes = a->cu_seqlens ? (((int64_t)a->N + 2) * 4 + 255) / 256 * 256 : 0;
+  return KDA_OK;
+}
+
 int run_intra(const kda::Params& p, hipStream_t s) {
   if (p.max_chunks * p.HV == 0) return KDA_OK;
-  int st = hip_status(p.cu ? kda::launch_chunk_table(p, s) : kda::launch_prep(p, s));
+  int st = hip_status(p.cu ? kda::launch_chunk_table(p.cu, p.N, p.T, p.max_chunks, p.table, p.counter, s) : kda::launch_prep(p, s));
   if (st != KDA_OK) return st;
   return hip_status(kda::launch_intra(p, s));
 }
@@ -159,6 +185,57 @@ int kda_debug_unpack(const kda_fwd_args* a, void* qg, void* w, void* kg, void* a
     if (!aligned(ptr, 16)) return KDA_ERR_INVALID_ARG;
   return hip_status(kda::launch_unpack(p, (uint16_t*)qg, (uint16_t*)w, (uint16_t*)kg, (uint16_t*)aqk,
                                        (uint16_t*)tmb, alpha, (hipStream_t)a->stream));
+}
+
+int kda_bwd_dhu_workspace_bytes(const kda_bwd_dhu_args* a, size_t* bytes) {
+  if (!bytes) return KDA_ERR_INVALID_ARG;
+  int64_t n = 0;
+  int st = check_bwd_shapes(a, &n);
+  if (st != KDA_OK) return st;
+  *bytes = (size_t)n;
+  return KDA_OK;
+}
+
+int kda_bwd_dhu(const kda_bwd_dhu_args* a) {
+  int64_t ws = 0;
+  int st = check_bwd_shapes(a, &ws);
+  if (st != KDA_OK) return st;
+  if ((int64_t)a->B * a->T > 0 && (!a->qg || !a->kg || !a->w || !a->g2 || !a->dout || !a->dv2))
+    return KDA_ERR_INVALID_ARG;
+  const void* a16[] = {a->qg, a->kg, a->w, a->g2, a->dht, a->dh0, a->dhc};
+  for (const void* ptr : a16)
+    if (!aligned(ptr, 16)) return KDA_ERR_INVALID_ARG;
+  const void* a8[] = {a->dout, a->dv, a->dv2, a->cu_seqlens};
+  for (const void* ptr : a8)
+    if (!aligned(ptr, 8)) return KDA_ERR_INVALID_ARG;
+  if (a->flags & ~(uint32_t)(KDA_FLAG_STATE_BF16 | KDA_FLAG_CKPT_BF16)) return KDA_ERR_INVALID_ARG;
+  if (ws > 0 && (!a->workspace || !aligned(a->workspace, 256) || a->workspace_bytes < (size_t)ws))
+    return KDA_ERR_WORKSPACE;
+  if (!(a->scale == a->scale)) return KDA_ERR_INVALID_ARG;
+  kda::BwdParams p;
+  p.qg = (const uint16_t*)a->qg;
+  p.kg = (const uint16_t*)a->kg;
+  p.w = (const uint16_t*)a->w;
+  p.g2 = a->g2;
+  p.dout = (const uint16_t*)a->dout;
+  p.dv = (const uint16_t*)a->dv;
+  p.dht = a->dht;
+  p.cu = a->cu_seqlens;
+  p.dv2 = (uint16_t*)a->dv2;
+  p.dh0 = a->dh0;
+  p.dhc = a->dhc;
+  p.table = a->cu_seqlens ? (int32_t*)a->workspace : nullptr;
+  p.scale = a->scale;
+  p.flags = a->flags;
+  p.B = a->B; p.T = a->T; p.HV = a->HV; p.K = a->K; p.V = a->V; p.N = a->N;
+  p.NT = (int)(((int64_t)a->T + kda::BT - 1) / kda::BT);
+  hipStream_t s = (hipStream_t)a->stream;
+  if (a->cu_seqlens) {
+    const int64_t cap = p.NT + (int64_t)p.N;   // upper bound on the chunk count
+    st = hip_status(kda::launch_chunk_table(p.cu, p.N, p.T, cap, p.table, nullptr, s));
+    if (st != KDA_OK) return st;
+  }
+  return hip_status(kda::launch_bwd_dhu(p, s));
 }
 
 const char* kda_strerror(int status) {

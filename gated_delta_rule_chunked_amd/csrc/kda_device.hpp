@@ -33,6 +33,10 @@ __device__ __forceinline__ f32x4 mfma16x4f32(float a, float b, f32x4 c) {
 }
 
 // ------------------------------------------------------------------ bf16
+// Bits of a float, taken by value.  With this compiler, __builtin_bit_cast applied
+// directly to an ext_vector element (v[i]) reads element 0 whatever i is, so
+// vector elements go through this copy.
+__device__ __forceinline__ uint32_t f2u(float x) { return __builtin_bit_cast(uint32_t, x); }
 __device__ __forceinline__ float bf2f(uint16_t b) {
   return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
@@ -110,6 +114,55 @@ __device__ __forceinline__ bf16x8 pfrag(const uint16_t* row, int base, int g) {
 // Two C-layout tiles (4 floats each) -> one packed P-order fragment.
 __device__ __forceinline__ uint4 pack_pair(const f32x4& lo, const f32x4& hi) {
   return make_uint4(pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(hi[0], hi[1]), pack2(hi[2], hi[3]));
+}
+
+// ------------------------------------------------------- scan helpers
+// Raw barrier: the wave's own LDS writes complete, then s_barrier, with a compiler
+// memory clobber.  __syncthreads would also wait for every outstanding global load
+// of the wave, which would serialize the register rings.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// State tensors are fp32, or bf16 when `bf16` is set.
+__device__ __forceinline__ float load_state(bool bf16, const void* base, int64_t idx) {
+  return bf16 ? bf2f(static_cast<const uint16_t*>(base)[idx]) : static_cast<const float*>(base)[idx];
+}
+__device__ __forceinline__ void store_state(bool bf16, void* base, int64_t idx, float x) {
+  if (bf16) static_cast<uint16_t*>(base)[idx] = f2bf(x);
+  else static_cast<float*>(base)[idx] = x;
+}
+
+__device__ __forceinline__ uint2 pack4(const f32x4& a) {
+  return make_uint2(pack2(a[0], a[1]), pack2(a[2], a[3]));
+}
+__device__ __forceinline__ bf16x8 cat(const uint2& lo, const uint2& hi) {
+  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+__device__ __forceinline__ uint2 lds8(const uint8_t* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// One sequence of a scan workgroup: batch row, first row, length, and the index
+// of its first chunk in the chunk numbering shared by the per-chunk outputs.
+struct SeqLoc {
+  int b;
+  int64_t bos;
+  int len;
+  int64_t cbase;  // chunk index of the sequence's first chunk
+};
+
+// ds_read_b64_tr_b16, the gfx950 LDS transpose read (8 bytes per lane).  Within
+// each block of 16 lanes, lane 4a + e receives as its element j (a, e, j = 0..3)
+// element e of the 8 bytes addressed by lane 4j + a of the block (lane layout
+// measured on gfx950).  On a row-major 16-bit tile, with lane (b = l/16, j, a) of
+// the wave addressing row row0 + 4b + j, columns col0 + 4a .. +3, lane (g, r)
+// receives rows row0 + 4g .. +3 of column col0 + r: a 16x16 C-layout tile, or the
+// low (high) half of a P-order fragment that contracts over the tile's rows.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_tr8(const uint8_t* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(uint2, v);
 }
 
 // ---------------------------------------------------- workspace records

@@ -63,42 +63,10 @@ struct OutOps {                            // output-wave operands of one phase
   uint2 v;                                 // chunk p+1: 4 columns of one token row of v
 };
 
-struct SeqLoc {
-  int b;
-  int64_t bos;
-  int len;
-  int64_t cbase;  // chunk index of the sequence's first chunk
-};
-
 template <int K>
 __device__ __forceinline__ const uint8_t* rec_ptr(const Params& p, const SeqLoc& sq, int hv, int c) {
   return p.recs + rec_index(hv, sq.cbase + c, p.max_chunks) * (int64_t)Rec<K>::BYTES;
 }
-
-// Raw barrier: the wave's own LDS writes complete, then s_barrier, with a compiler
-// memory clobber.  __syncthreads would also wait for every outstanding global load
-// of the wave, which would serialize the register rings.
-__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// States (h0, ht, hc) are fp32, or bf16 with FLAG_STATE_BF16.
-__device__ __forceinline__ float load_state(const Params& p, const void* base, int64_t idx) {
-  return (p.flags & FLAG_STATE_BF16) ? bf2f(static_cast<const uint16_t*>(base)[idx]) : static_cast<const float*>(base)[idx];
-}
-__device__ __forceinline__ void store_state(const Params& p, void* base, int64_t idx, float x) {
-  if (p.flags & FLAG_STATE_BF16) static_cast<uint16_t*>(base)[idx] = f2bf(x);
-  else static_cast<float*>(base)[idx] = x;
-}
-
-__device__ __forceinline__ uint2 pack4(const f32x4& a) {
-  return make_uint2(pack2(a[0], a[1]), pack2(a[2], a[3]));
-}
-__device__ __forceinline__ bf16x8 cat(const uint2& lo, const uint2& hi) {
-  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-}
-__device__ __forceinline__ uint2 lds8(const uint8_t* p) { return *reinterpret_cast<const uint2*>(p); }
-__device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 template <int K>
 __global__ __launch_bounds__(INTER_THREADS, 1) void inter_kernel(Params p, int n_items) {
@@ -127,7 +95,7 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void inter_kernel(Params p, int n
       const float qnan = __builtin_nanf("");
       if (p.ht)
         for (int idx = tid; idx < K * BV; idx += INTER_THREADS)
-          store_state(p, p.ht, (((int64_t)n * p.HV + hv) * K + idx / BV) * p.V + vt * BV + idx % BV, qnan);
+          store_state(p.flags & FLAG_STATE_BF16, p.ht, (((int64_t)n * p.HV + hv) * K + idx / BV) * p.V + vt * BV + idx % BV, qnan);
       const int64_t total = (int64_t)p.B * p.T * p.HV * p.V;
       for (int64_t idx = (int64_t)item * INTER_THREADS + tid; idx < total; idx += (int64_t)n_items * INTER_THREADS)
         p.o[idx] = 0x7fc0;
@@ -149,7 +117,7 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void inter_kernel(Params p, int n
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int d = 16 * md + 4 * g + rr;
-        h[md][rr] = p.h0 ? load_state(p, p.h0, (((int64_t)n * p.HV + hv) * K + d) * p.V + vt * BV + r) : 0.f;
+        h[md][rr] = p.h0 ? load_state(p.flags & FLAG_STATE_BF16, p.h0, (((int64_t)n * p.HV + hv) * K + d) * p.V + vt * BV + r) : 0.f;
       }
     barrier_lds();  // S0
     for (int ph = 0; ph < nphase; ++ph) {
@@ -245,7 +213,7 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void inter_kernel(Params p, int n
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int d = 16 * md + 4 * g + rr;
-          store_state(p, p.ht, (((int64_t)n * p.HV + hv) * K + d) * p.V + vt * BV + r, h[md][rr]);
+          store_state(p.flags & FLAG_STATE_BF16, p.ht, (((int64_t)n * p.HV + hv) * K + d) * p.V + vt * BV + r, h[md][rr]);
         }
     }
   } else if (wave <= 4) {

@@ -7,9 +7,10 @@
 
 namespace kda {
 
-// kda_fwd_args.flags bits (same values as KDA_FLAG_* in include/kda.h)
+// kda_fwd_args.flags / kda_bwd_dhu_args.flags bits (same values as KDA_FLAG_* in include/kda.h)
 constexpr uint32_t FLAG_BETA_LOGITS = 1u;
 constexpr uint32_t FLAG_STATE_BF16 = 2u;
+constexpr uint32_t FLAG_CKPT_BF16 = 4u;
 
 struct Params {
   const uint16_t* q;
@@ -32,11 +33,34 @@ struct Params {
   int64_t max_chunks;    // workspace capacity in chunks (per value head)
 };
 
+// Reverse state scan of the backward (kda_bwd_dhu).
+struct BwdParams {
+  const uint16_t* qg;    // bf16 [B, T, HV, K]
+  const uint16_t* kg;
+  const uint16_t* w;
+  const float* g2;       // fp32 [B, T, HV, K], chunk-local cumsum of g in log2 units
+  const uint16_t* dout;  // bf16 [B, T, HV, V]
+  const uint16_t* dv;    // bf16 [B, T, HV, V] or nullptr (zero)
+  const void* dht;       // state dtype, or nullptr
+  const int64_t* cu;
+  uint16_t* dv2;         // bf16 [B, T, HV, V]
+  void* dh0;             // state dtype, or nullptr
+  void* dhc;             // checkpoint dtype, or nullptr
+  int32_t* table;        // varlen chunk table (workspace) or nullptr
+  float scale;
+  uint32_t flags;        // FLAG_STATE_BF16, FLAG_CKPT_BF16
+  int B, T, HV, K, V, N;
+  int NT;                // fixed length: chunks per sequence
+};
+
 // Host launchers (return the hipError_t of the launch).
-hipError_t launch_chunk_table(const Params& p, hipStream_t s);   // varlen: also zeroes the counter
+// varlen chunk table (chunk_base[N+1], error flag at [N+1]); also zeroes *counter when non-null
+hipError_t launch_chunk_table(const int64_t* cu, int N, int T, int64_t max_chunks, int32_t* table,
+                              int32_t* counter, hipStream_t s);
 hipError_t launch_prep(const Params& p, hipStream_t s);          // fixed length: zeroes the counter
 hipError_t launch_intra(const Params& p, hipStream_t s);
 hipError_t launch_inter(const Params& p, hipStream_t s);
+hipError_t launch_bwd_dhu(const BwdParams& p, hipStream_t s);
 hipError_t launch_unpack(const Params& p, uint16_t* qg, uint16_t* w, uint16_t* kg,
                          uint16_t* aqk, uint16_t* tmb, float* alpha, hipStream_t s);
 

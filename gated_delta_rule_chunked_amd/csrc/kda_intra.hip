@@ -93,22 +93,23 @@ __device__ __forceinline__ bool locate_chunk(const Params& p, int64_t gc, ChunkL
 // One workgroup: chunk_base[n] = sum_{m<n} ceil(len_m / 64) (the tile_base of the
 // FlashKDA walkthrough's sequence-information section), chunk_base[N] = total,
 // and an error flag at [N+1] if cu_seqlens is not 0 = cu[0] <= ... <= cu[N] = T.
-__global__ __launch_bounds__(256) void chunk_table_kernel(Params p) {
+__global__ __launch_bounds__(256) void chunk_table_kernel(const int64_t* cu, int N, int T, int64_t max_chunks,
+                                                           int32_t* table, int32_t* counter) {
   __shared__ int32_t scan[256];
   __shared__ int32_t bad_any;
   const int tid = threadIdx.x;
   if (tid == 0) {
-    bad_any = (p.cu[0] != 0 || p.cu[p.N] != p.T) ? 1 : 0;
-    *p.counter = 0;   // work counter of the intra stage
+    bad_any = (cu[0] != 0 || cu[N] != T) ? 1 : 0;
+    if (counter) *counter = 0;   // work counter of the intra stage
   }
   __syncthreads();
   int32_t running = 0;
-  for (int base = 0; base < p.N; base += 256) {
+  for (int base = 0; base < N; base += 256) {
     const int n = base + tid;
     int32_t cnt = 0;
-    if (n < p.N) {
-      const int64_t a = p.cu[n], e = p.cu[n + 1];
-      if (a < 0 || e < a || e > p.T) atomicOr(&bad_any, 1);
+    if (n < N) {
+      const int64_t a = cu[n], e = cu[n + 1];
+      if (a < 0 || e < a || e > T) atomicOr(&bad_any, 1);
       else cnt = (int32_t)((e - a + BT - 1) / BT);
     }
     scan[tid] = cnt;
@@ -119,13 +120,13 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(Params p) {
       scan[tid] += add;
       __syncthreads();
     }
-    if (n < p.N) p.table[n] = running + scan[tid] - cnt;
+    if (n < N) table[n] = running + scan[tid] - cnt;
     running += scan[255];
     __syncthreads();
   }
   if (tid == 0) {
-    p.table[p.N] = running;
-    p.table[p.N + 1] = (bad_any || running > p.max_chunks) ? 1 : 0;
+    table[N] = running;
+    table[N + 1] = (bad_any || running > max_chunks) ? 1 : 0;
   }
 }
 
@@ -583,8 +584,9 @@ __global__ __launch_bounds__(NTHREADS) void unpack_kernel(Params p, int n_items,
 // ------------------------------------------------------------ launchers
 static int padded8(int64_t n) { return (int)((n + 7) / 8 * 8); }
 
-hipError_t launch_chunk_table(const Params& p, hipStream_t s) {
-  hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, s, p);
+hipError_t launch_chunk_table(const int64_t* cu, int N, int T, int64_t max_chunks, int32_t* table,
+                              int32_t* counter, hipStream_t s) {
+  hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, s, cu, N, T, max_chunks, table, counter);
   return hipGetLastError();
 }
 

@@ -22,9 +22,10 @@ KDA_ERR_HIP = -4
 KDA_CHUNK = 64
 KDA_FLAG_BETA_LOGITS = 1
 KDA_FLAG_STATE_BF16 = 2
+KDA_FLAG_CKPT_BF16 = 4
 
 EXPORTED = ("kda_fwd_workspace_bytes", "kda_fwd", "kda_fwd_intra", "kda_fwd_inter",
-            "kda_debug_unpack", "kda_strerror")
+            "kda_debug_unpack", "kda_bwd_dhu_workspace_bytes", "kda_bwd_dhu", "kda_strerror")
 
 
 class KdaFwdArgs(ctypes.Structure):
@@ -38,6 +39,19 @@ class KdaFwdArgs(ctypes.Structure):
         ("workspace", c_void_p), ("workspace_bytes", c_size_t),
         ("stream", c_void_p),
         ("flags", ctypes.c_uint32), ("hc", c_void_p),
+    ]
+
+
+class KdaBwdDhuArgs(ctypes.Structure):
+    """Mirror of ``kda_bwd_dhu_args`` (field order and types as in the header)."""
+    _fields_ = [
+        ("qg", c_void_p), ("kg", c_void_p), ("w", c_void_p), ("g2", c_void_p),
+        ("dout", c_void_p), ("dv", c_void_p), ("dht", c_void_p),
+        ("scale", c_float), ("cu_seqlens", c_void_p),
+        ("B", c_int32), ("T", c_int32), ("HV", c_int32), ("K", c_int32), ("V", c_int32), ("N", c_int32),
+        ("dv2", c_void_p), ("dh0", c_void_p), ("dhc", c_void_p),
+        ("workspace", c_void_p), ("workspace_bytes", c_size_t),
+        ("stream", c_void_p), ("flags", ctypes.c_uint32),
     ]
 
 
@@ -66,6 +80,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_fwd_workspace_bytes.restype = c_int
     lib.kda_debug_unpack.argtypes = [P] + [c_void_p] * 6
     lib.kda_debug_unpack.restype = c_int
+    PB = ctypes.POINTER(KdaBwdDhuArgs)
+    lib.kda_bwd_dhu_workspace_bytes.argtypes = [PB, ctypes.POINTER(c_size_t)]
+    lib.kda_bwd_dhu_workspace_bytes.restype = c_int
+    lib.kda_bwd_dhu.argtypes = [PB]
+    lib.kda_bwd_dhu.restype = c_int
     lib.kda_strerror.argtypes = [c_int]
     lib.kda_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -202,3 +221,92 @@ def kda_debug_unpack(args: KdaFwdArgs, qg=None, w=None, kg=None, aqk=None, tmb=N
                                          _ptr(tmb), _ptr(alpha))
     if st != KDA_OK:
         raise KdaError(st, "kda_debug_unpack")
+
+
+def make_bwd_args(qg, kg, w, g2, do, dv=None, dht=None, scale=None, cu_seqlens=None, dv2=None, dh0=None,
+                  dhc=None, workspace=None, stream=None, flags=0) -> KdaBwdDhuArgs:
+    """Fill ``kda_bwd_dhu_args`` from torch tensors (shapes as in the header).
+
+    qg, kg, w: [B, T, HV, K] bf16; g2: [B, T, HV, K] fp32; do, dv, dv2: [B, T, HV, V]
+    bf16; dht, dh0: [N, HV, K, V] fp32 (bf16 with KDA_FLAG_STATE_BF16); dhc:
+    [C, HV, K, V] fp32 (bf16 with KDA_FLAG_CKPT_BF16).  Only pointers and sizes are read.
+    """
+    import torch
+    B, T, HV, K = qg.shape
+    V = do.shape[3]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    sdt = torch.bfloat16 if flags & KDA_FLAG_STATE_BF16 else torch.float32
+    cdt = torch.bfloat16 if flags & KDA_FLAG_CKPT_BF16 else torch.float32
+    bf = torch.bfloat16
+    for name, t, dt in (("qg", qg, bf), ("kg", kg, bf), ("w", w, bf), ("g2", g2, torch.float32),
+                        ("do", do, bf), ("dv", dv, bf), ("dht", dht, sdt), ("cu_seqlens", cu_seqlens, torch.int64),
+                        ("dv2", dv2, bf), ("dh0", dh0, sdt), ("dhc", dhc, cdt)):
+        if t is not None:
+            if t.dtype != dt:
+                raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+    if stream is None:
+        stream = torch.cuda.current_stream(qg.device).cuda_stream
+    a = KdaBwdDhuArgs()
+    a.qg, a.kg, a.w, a.g2 = _ptr(qg), _ptr(kg), _ptr(w), _ptr(g2)
+    a.dout, a.dv, a.dht = _ptr(do), _ptr(dv), _ptr(dht)
+    a.scale = float(K ** -0.5 if scale is None else scale)
+    a.cu_seqlens = _ptr(cu_seqlens)
+    a.B, a.T, a.HV, a.K, a.V, a.N = B, T, HV, K, V, N
+    a.dv2, a.dh0, a.dhc = _ptr(dv2), _ptr(dh0), _ptr(dhc)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    a.stream = stream
+    a.flags = int(flags)
+    return a
+
+
+def kda_bwd_dhu_workspace_bytes(args: KdaBwdDhuArgs) -> int:
+    n = c_size_t(0)
+    st = load_library().kda_bwd_dhu_workspace_bytes(ctypes.byref(args), ctypes.byref(n))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_bwd_dhu_workspace_bytes")
+    return n.value
+
+
+def kda_bwd_dhu_raw(args: KdaBwdDhuArgs) -> None:
+    st = load_library().kda_bwd_dhu(ctypes.byref(args))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_bwd_dhu")
+
+
+def kda_bwd_dhu(qg, kg, w, g2, do, dv=None, dht=None, scale=None, cu_seqlens=None, state_dtype=None,
+                checkpoint_dtype=None, output_dh0=True, output_checkpoints=True):
+    """Reverse state scan of the chunked backward on the current stream.
+
+    Returns (dv2, dhc or None, dh0 or None): dv2 [B, T, HV, V] bf16, dhc [C, HV, K, V]
+    (``checkpoint_dtype``: torch.float32 default, or torch.bfloat16) the gradient of
+    the state after each chunk (see ``num_chunks``), dh0 [N, HV, K, V] in
+    ``state_dtype`` (torch.float32 default, or torch.bfloat16; dht must match).
+    """
+    import torch
+    if not qg.is_cuda:
+        raise RuntimeError("kda_bwd_dhu runs on the GPU only (tensors must be on a HIP device)")
+    load_library()
+    B, T, HV, K = qg.shape
+    V = do.shape[3]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    sdt = torch.float32 if state_dtype is None else state_dtype
+    cdt = torch.float32 if checkpoint_dtype is None else checkpoint_dtype
+    for name, dt in (("state_dtype", sdt), ("checkpoint_dtype", cdt)):
+        if dt not in (torch.float32, torch.bfloat16):
+            raise TypeError(f"{name} must be torch.float32 or torch.bfloat16")
+    flags = (KDA_FLAG_STATE_BF16 if sdt == torch.bfloat16 else 0) | (KDA_FLAG_CKPT_BF16 if cdt == torch.bfloat16 else 0)
+    dv2 = torch.empty((B, T, HV, V), dtype=torch.bfloat16, device=qg.device)
+    dh0 = torch.empty((N, HV, K, V), dtype=sdt, device=qg.device) if output_dh0 else None
+    dhc = None
+    if output_checkpoints:
+        dhc = torch.empty((num_chunks(T, cu_seqlens, B), HV, K, V), dtype=cdt, device=qg.device)
+    args = make_bwd_args(qg, kg, w, g2, do, dv, dht, scale, cu_seqlens, dv2, dh0, dhc, flags=flags)
+    n = kda_bwd_dhu_workspace_bytes(args)
+    workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=qg.device)
+    args.workspace = workspace.data_ptr()
+    args.workspace_bytes = workspace.numel()
+    kda_bwd_dhu_raw(args)
+    return dv2, dhc, dh0

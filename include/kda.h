@@ -52,6 +52,10 @@ extern "C" {
  * "KDA源码剖析之FlashKDA（下）", parameter list of the forward entry point). */
 #define KDA_FLAG_BETA_LOGITS  1u  /* beta holds raw logits; the kernel applies the sigmoid */
 #define KDA_FLAG_STATE_BF16   2u  /* h0, ht and hc are bf16 instead of fp32                */
+/* Option bit of kda_bwd_dhu_args.flags (with KDA_FLAG_STATE_BF16 for dht / dh0):
+ * the per-chunk gradient checkpoints dhc are bf16, the checkpoint format of the
+ * kernel-fun bwd_dhu page (host wrapper), instead of fp32. */
+#define KDA_FLAG_CKPT_BF16    4u
 
 typedef struct kda_fwd_args {
   /* Inputs (device, bf16 unless stated).
@@ -136,6 +140,67 @@ int kda_fwd_inter(const kda_fwd_args* a);
  * Rows of each sequence are written; other memory is untouched. */
 int kda_debug_unpack(const kda_fwd_args* a, void* qg, void* w, void* kg, void* aqk,
                      void* tmb, float* alpha);
+
+/* ------------------------------------------------------------------------
+ * Reverse state scan of the chunked backward pass ("kernel-fun 0.2.0.dev1 --
+ * kernel_fun/kda/_kernels/bwd_dhu.py", module docstring and host wrapper).  For a
+ * loss with gradient do of o and dht of the final state, per sequence and value
+ * head, dh starts at dht (or 0) and walks the chunks newest first:
+ *     dhc[c] = dh                                   (gradient of the state after chunk c)
+ *     dv2    = kg dh + dv                            (per token row of the chunk)
+ *     dh    <- diag(exp2 gd) dh + scale qg^T do - w^T dv2,   gd = g2 at the chunk's last row
+ * and dh0 = dh after the sequence's first chunk.  Chunks are 64 tokens and restart
+ * at every sequence start, as in the forward.  Conventions as for kda_fwd_args.
+ */
+typedef struct kda_bwd_dhu_args {
+  /* Inputs (device).  The forward's chunk operands, recomputed by the caller:
+   *   qg  : bf16 [B, T, HV, K]  q * exp2(g2)                (no scale folded in)
+   *   kg  : bf16 [B, T, HV, K]  k * exp2(g2_last - g2)      (g2_last: the chunk's last valid row)
+   *   w   : bf16 [B, T, HV, K]  Tm diag(beta) (k * exp2(g2)), the forward's w
+   *   g2  : fp32 [B, T, HV, K]  chunk-local inclusive cumsum of g in log2 units
+   *         (G / ln 2); only each chunk's last valid row is read
+   *   dout: bf16 [B, T, HV, V]  gradient of o
+   *   dv  : bf16 [B, T, HV, V]  the part of the gradient of v' that does not pass
+   *         through the state (Aqk^T do per chunk), or NULL for zero
+   *   dht : [N, HV, K, V] gradient of the final state (fp32, bf16 with
+   *         KDA_FLAG_STATE_BF16), or NULL for zero
+   *   cu_seqlens, B, T, HV, K, V, N: as in kda_fwd_args (K in {64, 128}, V a
+   *         positive multiple of 16; varlen: B == 1). */
+  const void* qg;
+  const void* kg;
+  const void* w;
+  const float* g2;
+  const void* dout;
+  const void* dv;
+  const void* dht;
+  float scale;                 /* usually K^-0.5                                      */
+  const int64_t* cu_seqlens;
+  int32_t B, T, HV, K, V, N;
+  /* Outputs (device, caller-allocated).
+   *   dv2 : bf16 [B, T, HV, V]  every row of every sequence is written
+   *   dh0 : [N, HV, K, V] (dht's dtype), or NULL to skip
+   *   dhc : [C, HV, K, V] fp32 (bf16 with KDA_FLAG_CKPT_BF16), chunks numbered as
+   *         hc of kda_fwd_args, or NULL to skip
+   * Alignment (else KDA_ERR_INVALID_ARG): qg, kg, w, g2, dht, dh0, dhc 16 bytes;
+   * dout, dv, dv2 and cu_seqlens 8 bytes. */
+  void* dv2;
+  void* dh0;
+  void* dhc;
+  /* Scratch (device, 256-byte aligned, size from kda_bwd_dhu_workspace_bytes;
+   * zero bytes, so NULL is allowed, for fixed length). */
+  void* workspace;
+  size_t workspace_bytes;
+  void* stream;                /* hipStream_t */
+  uint32_t flags;              /* KDA_FLAG_STATE_BF16 | KDA_FLAG_CKPT_BF16; others rejected */
+} kda_bwd_dhu_args;
+
+/* Workspace size for these arguments (host only; reads the shape fields and
+ * whether cu_seqlens is NULL). */
+int kda_bwd_dhu_workspace_bytes(const kda_bwd_dhu_args* a, size_t* bytes);
+
+/* The reverse state scan: dv2, dh0 and dhc from qg, kg, w, g2, dout, dv, dht.
+ * Rejected cu_seqlens (checked on the device) fill dv2 and dh0 with NaN. */
+int kda_bwd_dhu(const kda_bwd_dhu_args* a);
 
 /* Static text for a status code, or for the last HIP error seen by this thread
  * when status == KDA_ERR_HIP. */

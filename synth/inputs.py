@@ -131,3 +131,15 @@ def make_config_inputs(cfg_id: int) -> dict:
                     n_varlen=w.n_varlen, varlen_range=w.varlen_range)
     d["name"] = w.name
     return d
+
+
+def make_grads(d: dict, seed: int, has_dht: bool = True) -> dict:
+    """Seeded gradients for a backward pass over the inputs ``d`` (own rng, so the
+    forward inputs are unchanged): do ~ N(0, 1) rounded to bfloat16, shaped like v;
+    dht ~ 0.1 N(0, 1) rounded to float32, shaped like h0 ([N, HV, K, V]), or None."""
+    rng = np.random.default_rng(seed)
+    do = round_to_bf16(rng.standard_normal(np.shape(d["v"]))).astype(np.float32)
+    dht = None
+    if has_dht:
+        dht = (0.1 * rng.standard_normal((d["N"], d["HV"], d["K"], d["V"]))).astype(np.float32)
+    return dict(do=do, dht=dht)

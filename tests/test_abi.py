@@ -125,3 +125,62 @@ def test_null_args_and_strerror(lib):
     assert lib.kda_fwd(None) == K.KDA_ERR_INVALID_ARG
     assert lib.kda_fwd_workspace_bytes(None, None) == K.KDA_ERR_INVALID_ARG
     assert K.kda_strerror(0) == "ok" and K.kda_strerror(12345) == "unknown status"
+
+
+# ---------------------------------------------------------------- backward scan
+def test_bwd_struct_layout_matches_header():
+    a = K.KdaBwdDhuArgs
+    assert a.g2.offset == 24 and a.dht.offset == 48 and a.scale.offset == 56 and a.cu_seqlens.offset == 64
+    assert a.B.offset == 72 and a.N.offset == 92 and a.dv2.offset == 96 and a.dhc.offset == 112
+    assert a.workspace_bytes.offset == 128 and a.stream.offset == 136 and a.flags.offset == 144
+    assert ctypes.sizeof(a) == 152
+
+
+def bwd_args(**over):
+    a = K.KdaBwdDhuArgs()
+    fake = 1 << 20
+    a.qg = a.kg = a.w = a.g2 = a.dout = a.dv2 = fake
+    a.scale = 0.125
+    a.B, a.T, a.HV, a.K, a.V, a.N = 1, 256, 4, 128, 128, 1
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def bwd_ws(a):
+    n = ctypes.c_size_t(0)
+    st = K.load_library().kda_bwd_dhu_workspace_bytes(ctypes.byref(a), ctypes.byref(n))
+    return st, n.value
+
+
+def test_bwd_workspace_bytes(lib):
+    # fixed length needs no scratch; varlen holds the chunk table (N + 2 int32)
+    assert bwd_ws(bwd_args(B=1, T=8192, HV=32)) == (0, 0)
+    assert bwd_ws(bwd_args(N=5, cu_seqlens=1 << 20)) == (0, 256)
+    assert bwd_ws(bwd_args(N=70, cu_seqlens=1 << 20)) == (0, 512)
+    assert bwd_ws(bwd_args(K=96))[0] == K.KDA_ERR_UNSUPPORTED
+    assert lib.kda_bwd_dhu_workspace_bytes(None, None) == K.KDA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(K=96), K.KDA_ERR_UNSUPPORTED),
+    (dict(V=24), K.KDA_ERR_UNSUPPORTED),
+    (dict(B=0), K.KDA_ERR_INVALID_ARG),
+    (dict(N=2), K.KDA_ERR_INVALID_ARG),
+    (dict(B=2, N=2, cu_seqlens=1 << 20), K.KDA_ERR_INVALID_ARG),
+    (dict(qg=0), K.KDA_ERR_INVALID_ARG),
+    (dict(g2=0), K.KDA_ERR_INVALID_ARG),
+    (dict(dv2=0), K.KDA_ERR_INVALID_ARG),
+    (dict(w=(1 << 20) + 8), K.KDA_ERR_INVALID_ARG),       # K-wide operands need 16 bytes
+    (dict(dout=(1 << 20) + 4), K.KDA_ERR_INVALID_ARG),    # V-wide tensors need 8 bytes
+    (dict(dhc=(1 << 20) + 8), K.KDA_ERR_INVALID_ARG),
+    (dict(dht=(1 << 20) + 8), K.KDA_ERR_INVALID_ARG),
+    (dict(flags=1), K.KDA_ERR_INVALID_ARG),               # the forward's beta option
+    (dict(flags=8), K.KDA_ERR_INVALID_ARG),
+    (dict(N=5, cu_seqlens=1 << 20), K.KDA_ERR_WORKSPACE),  # varlen needs the table
+    (dict(N=5, cu_seqlens=1 << 20, workspace=1 << 20, workspace_bytes=100), K.KDA_ERR_WORKSPACE),
+    (dict(scale=float("nan")), K.KDA_ERR_INVALID_ARG),
+])
+def test_bwd_validation_rejects_before_launch(lib, over, status):
+    assert lib.kda_bwd_dhu(ctypes.byref(bwd_args(**over))) == status
+    assert lib.kda_bwd_dhu(None) == K.KDA_ERR_INVALID_ARG
