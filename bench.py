@@ -12,6 +12,15 @@ each plus beta 2 B = 1,282 B (q, k per q/k head), plus the final state ht once p
 (sequence, head).  The intra kernel necessarily reads q, k, g, beta (770 B); the
 inter kernel reads v and writes o (512 B) and ht.  Algorithmic flops per token
 and head: 180,224 (dense 64-row tiles).
+
+The backward's reverse state scan (kda_bwd_dhu) is timed on the same shape as a
+separate object (``bwd_dhu``), in the checkpoint format of the bwd_dhu page (bf16
+dhc, fp32 dht / dh0).  Its algorithmic bytes per token and value head: qg, kg, w
+read (768 B), do and dv read (512 B), dv2 written (256 B); per chunk and head the
+decay row (K fp32) read and the checkpoint (K x V bf16) written; dht read and dh0
+written once per (sequence, head).  Its inputs are synthetic stand-ins with the
+forward operands' shapes and magnitudes, built on the device outside the timed
+region (the scan's time does not depend on the values).
 """
 from __future__ import annotations
 
@@ -35,6 +44,7 @@ FLOPS_PER_TOKEN_HEAD = 180224
 KERNEL_SOURCES = {
     "intra": ["gated_delta_rule_chunked_amd/csrc/kda_intra.hip", "gated_delta_rule_chunked_amd/csrc/kda_device.hpp"],
     "inter": ["gated_delta_rule_chunked_amd/csrc/kda_inter.hip", "gated_delta_rule_chunked_amd/csrc/kda_device.hpp"],
+    "bwd_dhu": ["gated_delta_rule_chunked_amd/csrc/kda_bwd.hip", "gated_delta_rule_chunked_amd/csrc/kda_device.hpp"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
@@ -87,6 +97,59 @@ def cpu_baseline(d, budget_s=12.0):
                       f"(numpy, 1 thread), {dt:.1f} s; tokens/s of the full {d['HV']}-head layer"}
 
 
+def bwd_algorithmic_bytes(B, T, HV, K, V, N, C):
+    """Bytes one kda_bwd_dhu call must move (bf16 checkpoints, fp32 dht / dh0)."""
+    return (B * T * HV * (3 * K * 2 + 3 * V * 2)     # qg, kg, w; do, dv, dv2
+            + C * HV * (K * 4 + K * V * 2)          # decay row, checkpoint
+            + 2 * N * HV * K * V * 4)               # dht, dh0
+
+
+def bench_bwd(t, d, dev, stream, steps):
+    """Time kda_bwd_dhu at the workload's shape; returns the bwd_dhu object."""
+    import torch
+    from gated_delta_rule_chunked_amd import KDA_FLAG_CKPT_BF16, kda_bwd_dhu_raw, make_bwd_args, num_chunks
+    B, T, HV, K, V, N = d["B"], d["T"], d["HV"], d["K"], d["V"], d["N"]
+    NT = (T + 63) // 64
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(33)
+    # chunk-local cumsum of g in log2 units (T is a multiple of 64 here)
+    g = t["g"].float().reshape(B, NT, 64, HV, K)
+    g2 = (torch.cumsum(g, dim=2) * 1.4426950408889634).reshape(B, T, HV, K).contiguous()
+    last = g2.reshape(B, NT, 64, HV, K)[:, :, 63:].expand(B, NT, 64, HV, K).reshape(B, T, HV, K)
+    qh = t["q"].float().repeat_interleave(HV // d["HQK"], dim=2)
+    kh = t["k"].float().repeat_interleave(HV // d["HQK"], dim=2)
+    qg = (qh * torch.exp2(g2)).to(torch.bfloat16)
+    kg = (kh * torch.exp2(last - g2)).to(torch.bfloat16)
+    w = (kh * torch.exp2(g2) * t["beta"].float()[..., None]).to(torch.bfloat16)
+    do = torch.randn((B, T, HV, V), generator=gen, device=dev).to(torch.bfloat16)
+    dv = (0.1 * torch.randn((B, T, HV, V), generator=gen, device=dev)).to(torch.bfloat16)
+    dht = 0.1 * torch.randn((N, HV, K, V), generator=gen, device=dev)
+    C = num_chunks(T, None, B)
+    dv2 = torch.empty((B, T, HV, V), dtype=torch.bfloat16, device=dev)
+    dh0 = torch.empty((N, HV, K, V), dtype=torch.float32, device=dev)
+    dhc = torch.empty((C, HV, K, V), dtype=torch.bfloat16, device=dev)
+    a = make_bwd_args(qg, kg, w, g2, do, dv, dht, d["scale"], None, dv2, dh0, dhc, stream=stream.cuda_stream,
+                      flags=KDA_FLAG_CKPT_BF16)
+    for _ in range(3):
+        kda_bwd_dhu_raw(a)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        kda_bwd_dhu_raw(a)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    nbytes = bwd_algorithmic_bytes(B, T, HV, K, V, N, C)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    flops = 6 * K * V * B * T * HV       # DV, QD, WD per token and head
+    return {"ms": ms, "tokens_per_s": B * T / (ms * 1e-3), "algorithmic_bytes": nbytes,
+            "roofline": {"bound": "hbm", "kernel": "bwd_dhu", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for("bwd_dhu")},
+            "mfma_frac": flops / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+            "checkpoints": "bf16", "states": "fp32", "data": "synthetic stand-ins for qg, kg, w, g2, do, dv, dht"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,6 +158,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true", help="skip timing the forward's options")
     ap.add_argument("--cold", type=int, default=20, help="extra cold-cache steps (flush between)")
+    ap.add_argument("--no-bwd", action="store_true", help="skip timing the backward state scan")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -193,6 +257,8 @@ def main():
             variants_ms[name] = e0.elapsed_time(e1) / 10
         del hc, ht_bf
 
+    bwd = None if args.no_bwd else bench_bwd(t, d, dev, stream, args.steps)
+
     tokens = B * T
     value = tokens / (ms_per_step * 1e-3)
     ab_intra, ab_inter = algorithmic_bytes(d)
@@ -226,6 +292,7 @@ def main():
                           "mfma_frac": flops / (ms_per_step * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12)},
         "cold_cache_ms_per_step": cold_ms,
         "options_ms_per_step": variants_ms,
+        "bwd_dhu": bwd,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(d)
