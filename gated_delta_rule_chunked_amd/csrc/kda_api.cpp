@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/kda.h"
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
@@ -13,7 +15,7 @@
 static_assert(offsetof(kda_fwd_args, scale) == 40 && offsetof(kda_fwd_args, B) == 64 &&
                   offsetof(kda_fwd_args, o) == 96 && offsetof(kda_fwd_args, stream) == 128 &&
                   offsetof(kda_fwd_args, flags) == 136 && offsetof(kda_fwd_args, hc) == 144 &&
-                  sizeof(kda_fwd_args) == 152,
+                  offsetof(kda_fwd_args, seg_chunks) == 152 && sizeof(kda_fwd_args) == 160,
               "argument struct layout (mirrored by the Python binding)");
 static_assert(offsetof(kda_bwd_dhu_args, scale) == 56 && offsetof(kda_bwd_dhu_args, B) == 72 &&
                   offsetof(kda_bwd_dhu_args, dv2) == 96 && offsetof(kda_bwd_dhu_args, stream) == 136 &&
@@ -31,13 +33,27 @@ bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
 
 int64_t rec_bytes(int K) { return K == 128 ? kda::Rec<128>::BYTES : kda::Rec<64>::BYTES; }
 
+int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
+
 // Shape checks shared by every entry point.  Fills the layout on success.
+//
+// Choice of scan (kda_inter.hip or kda_scan.hip).  The 64-column workgroups of
+// kda_scan.hip stream a chunk's record once for four times the columns of the
+// 16-column workgroups of kda_inter.hip, so they are used whenever they alone fill
+// the compute units (every sequence is then one segment).  Otherwise the 16-column
+// scan is used when it has a workgroup for at least every other compute unit, or
+// when sequences are short; and else the segmented scan cuts each sequence into
+// segments of L chunks joined through the scan's affine dependence on its start
+// state, with L = max(8, ceil(chunks / 8)) (at most eight segments per sequence:
+// the full pass joins segment s through s - 1 small products).  A positive
+// seg_chunks selects kda_scan.hip with that L.
 int check_shapes(const kda_fwd_args* a, kda::WsLayout* L) {
   if (!a) return KDA_ERR_INVALID_ARG;
   if (a->K != 64 && a->K != 128) return KDA_ERR_UNSUPPORTED;
   if (a->V <= 0 || a->V % kda::BV != 0) return KDA_ERR_UNSUPPORTED;
   if (a->B < 1 || a->T < 0 || a->HQK < 1 || a->HV < 1 || a->N < 1) return KDA_ERR_INVALID_ARG;
   if (a->HV % a->HQK != 0) return KDA_ERR_INVALID_ARG;
+  if (a->seg_chunks < 0) return KDA_ERR_INVALID_ARG;
   if (a->cu_seqlens) {
     if (a->B != 1) return KDA_ERR_INVALID_ARG;
   } else if (a->N != a->B) {
@@ -49,13 +65,63 @@ int check_shapes(const kda_fwd_args* a, kda::WsLayout* L) {
   const int64_t nt = ((int64_t)a->T + kda::BT - 1) / kda::BT;
   const int64_t max_chunks = a->cu_seqlens ? nt + a->N : (int64_t)a->B * nt;
   if (max_chunks * a->HV >= ((int64_t)1 << 31) - 8) return KDA_ERR_INVALID_ARG;
-  if ((int64_t)a->N * a->HV * (a->V / kda::BV) >= ((int64_t)1 << 31) - 8) return KDA_ERR_INVALID_ARG;
+  const int64_t units16 = (int64_t)a->N * a->HV * (a->V / kda::BV);
+  if (units16 >= ((int64_t)1 << 31) - 8) return KDA_ERR_INVALID_ARG;
   if (a->N >= (1 << 30)) return KDA_ERR_INVALID_ARG;
+  // scan choice and segment plan
+  bool seg_path;
+  int64_t seg_L;
+  if (a->seg_chunks > 0) {
+    seg_path = true;
+    seg_L = a->seg_chunks;
+  } else {
+    const int64_t cus = kda::device_cus();
+    const int64_t units64 = (int64_t)a->N * a->HV * ((a->V + 63) / 64);
+    if (units64 >= cus) {            // 64-column workgroups alone fill the device: one segment each
+      seg_path = true;
+      seg_L = std::max<int64_t>(nt, 1);
+    } else {
+      seg_path = units16 * 2 < cus && nt >= 64;
+      seg_L = std::max<int64_t>(8, (nt + 7) / 8);
+    }
+  }
+  seg_L = std::min<int64_t>(seg_L, std::max<int64_t>(nt, 1));
+  int64_t seg_S = 1, max_segs = 0;
+  bool multi = false;
+  if (seg_path) {
+    if (a->cu_seqlens) {
+      // sum over sequences of max(1, ceil(nc / L)) <= chunks / L + N, chunks <= nt + N
+      max_segs = (nt + a->N) / seg_L + a->N;
+      multi = seg_L < nt;
+    } else {
+      seg_S = std::max<int64_t>(1, (nt + seg_L - 1) / seg_L);
+      max_segs = (int64_t)a->B * seg_S;
+      multi = seg_S > 1;
+    }
+    if (max_segs * a->HV * ((a->V + 63) / 64 + a->K / 64) >= ((int64_t)1 << 31) - 8) return KDA_ERR_INVALID_ARG;
+  }
+  L->seg_path = seg_path;
+  L->seg_L = (int)seg_L;
+  L->seg_S = (int)seg_S;
+  L->max_segs = max_segs;
   L->rec_bytes = rec_bytes(a->K);
   L->max_chunks = max_chunks;
   const int64_t recs = max_chunks * a->HV * L->rec_bytes;
-  L->table_bytes = recs == 0 ? 0 : (16 + (a->cu_seqlens ? ((int64_t)a->N + 2) * 4 : 0) + 255) / 256 * 256;
-  L->total_bytes = L->table_bytes + recs;
+  // header: counter | varlen: chunk table (N + 2) | segment table (N + 1, segmented scan) | chunk info
+  L->cinfo_off = 0;
+  int64_t head = 16;
+  if (a->cu_seqlens) {
+    head += ((int64_t)a->N + 2) * 4 + (seg_path ? ((int64_t)a->N + 1) * 4 : 0);
+    L->cinfo_off = (head + 7) / 8 * 8;
+    head = L->cinfo_off + max_chunks * 8;
+  }
+  L->table_bytes = recs == 0 ? 0 : round256(head);
+  const int64_t bbytes = multi ? max_segs * a->HV * a->K * a->V * 4 : 0;
+  const int64_t mbytes = multi ? max_segs * a->HV * a->K * a->K * 2 : 0;
+  // the segmented scan copies records in whole KiB: 1 KiB of slack after the last
+  L->b_off = recs == 0 ? 0 : round256(L->table_bytes + recs + (seg_path ? 1024 : 0));
+  L->m_off = L->b_off + bbytes;
+  L->total_bytes = L->m_off + mbytes;
   return KDA_OK;
 }
 
@@ -94,9 +160,18 @@ int check_call(const kda_fwd_args* a, int need, kda::Params* p) {
   p->ht = a->ht;
   p->hc = a->hc;
   p->flags = a->flags;
-  p->counter = (int32_t*)a->workspace;
-  p->table = a->cu_seqlens ? (int32_t*)((uint8_t*)a->workspace + 16) : nullptr;
-  p->recs = (uint8_t*)a->workspace + L.table_bytes;
+  uint8_t* ws = (uint8_t*)a->workspace;
+  p->counter = (int32_t*)ws;
+  p->table = a->cu_seqlens ? (int32_t*)(ws + 16) : nullptr;
+  p->segtab = (a->cu_seqlens && L.seg_path) ? (int32_t*)(ws + 16 + ((int64_t)a->N + 2) * 4) : nullptr;
+  p->cinfo = a->cu_seqlens ? (int2*)(ws + L.cinfo_off) : nullptr;
+  p->recs = ws + L.table_bytes;
+  p->bbuf = L.m_off > L.b_off ? (float*)(ws + L.b_off) : nullptr;
+  p->mbuf = L.total_bytes > L.m_off ? (uint16_t*)(ws + L.m_off) : nullptr;
+  p->seg_L = L.seg_L;
+  p->seg_S = L.seg_S;
+  p->max_segs = L.max_segs;
+  p->seg_path = L.seg_path;
   p->scale = a->scale;
   p->B = a->B; p->T = a->T; p->HQK = a->HQK; p->HV = a->HV; p->K = a->K; p->V = a->V; p->N = a->N;
   p->NT = (int)(((int64_t)a->T + kda::BT - 1) / kda::BT);
@@ -134,7 +209,9 @@ int check_bwd_shapes(const kda_bwd_dhu_args* a, int64_t* ws_bytes) {
 
 int run_intra(const kda::Params& p, hipStream_t s) {
   if (p.max_chunks * p.HV == 0) return KDA_OK;
-  int st = hip_status(p.cu ? kda::launch_chunk_table(p.cu, p.N, p.T, p.max_chunks, p.table, p.counter, s) : kda::launch_prep(p, s));
+  int st = hip_status(p.cu ? kda::launch_chunk_table(p.cu, p.N, p.T, p.max_chunks, p.table, p.counter, p.seg_L,
+                                                     p.max_segs, p.segtab, p.cinfo, s)
+                           : kda::launch_prep(p, s));
   if (st != KDA_OK) return st;
   return hip_status(kda::launch_intra(p, s));
 }
@@ -163,7 +240,7 @@ int kda_fwd_inter(const kda_fwd_args* a) {
   kda::Params p;
   int st = check_call(a, NEED_INTER, &p);
   if (st != KDA_OK) return st;
-  return hip_status(kda::launch_inter(p, (hipStream_t)a->stream));
+  return hip_status(p.seg_path ? kda::launch_scan(p, (hipStream_t)a->stream) : kda::launch_inter(p, (hipStream_t)a->stream));
 }
 
 int kda_fwd(const kda_fwd_args* a) {
@@ -172,7 +249,7 @@ int kda_fwd(const kda_fwd_args* a) {
   if (st != KDA_OK) return st;
   st = run_intra(p, (hipStream_t)a->stream);
   if (st != KDA_OK) return st;
-  return hip_status(kda::launch_inter(p, (hipStream_t)a->stream));
+  return hip_status(p.seg_path ? kda::launch_scan(p, (hipStream_t)a->stream) : kda::launch_inter(p, (hipStream_t)a->stream));
 }
 
 int kda_debug_unpack(const kda_fwd_args* a, void* qg, void* w, void* kg, void* aqk, void* tmb,
@@ -232,7 +309,7 @@ int kda_bwd_dhu(const kda_bwd_dhu_args* a) {
   hipStream_t s = (hipStream_t)a->stream;
   if (a->cu_seqlens) {
     const int64_t cap = p.NT + (int64_t)p.N;   // upper bound on the chunk count
-    st = hip_status(kda::launch_chunk_table(p.cu, p.N, p.T, cap, p.table, nullptr, s));
+    st = hip_status(kda::launch_chunk_table(p.cu, p.N, p.T, cap, p.table, nullptr, 1, 0, nullptr, nullptr, s));
     if (st != KDA_OK) return st;
   }
   return hip_status(kda::launch_bwd_dhu(p, s));

@@ -214,14 +214,24 @@ __device__ __host__ __forceinline__ constexpr int tri_frag(int mb, int s) {
 }
 __device__ __host__ __forceinline__ constexpr int tri_steps(int mb) { return mb < 2 ? 1 : 2; }
 
-// Layout of the workspace: [header | records].  Header: int32 work counter of the
-// intra stage at byte 0; for varlen, the chunk table (int32 chunk_base[N+1]) and an
-// int32 error flag from byte 16; padded to a multiple of 256 bytes.
+// Layout of the workspace: [header | records | 1 KiB pad | B | M].  Header: int32
+// work counter of the intra stage at byte 0; for varlen, the chunk table (int32
+// chunk_base[N+1]) and an int32 error flag from byte 16, then (segmented scan) the
+// segment table (int32 seg_base[N+1]) and, 8-byte aligned, int32 {first row, valid
+// rows} per chunk; padded to a multiple of 256 bytes.  The pad keeps the scan's
+// whole-KiB record copies inside the workspace.  B (fp32 [segments, HV, K, V]) and
+// M (bf16 [segments, HV, K, K]) hold the segmented scan's per-segment end states and
+// transitions; they are empty when no sequence has more than one segment.
 struct WsLayout {
-  int64_t table_bytes;
+  int64_t table_bytes;  // header: counter, varlen chunk table, segment table and chunk info
+  int64_t cinfo_off;    // varlen: byte offset of the per-chunk {first row, valid rows}
   int64_t rec_bytes;
   int64_t max_chunks;   // capacity in chunks per value head
+  int64_t b_off, m_off; // segment end states / transitions (0 bytes when every sequence is one segment)
   int64_t total_bytes;
+  bool seg_path;        // the segmented scan is used
+  int seg_L, seg_S;     // chunks per segment; fixed length: segments per sequence
+  int64_t max_segs;
 };
 
 }  // namespace kda

@@ -24,6 +24,7 @@ struct Params {
   void* ht;             // state dtype
   int32_t* table;        // varlen: chunk_base[N+1], then error flag at [N+1]
   int32_t* counter;      // work counter of the intra stage (zeroed by the prep kernel)
+  int2* cinfo;           // varlen: per chunk {first row, valid rows}, else nullptr
   void* hc;              // per-chunk states (state dtype) or nullptr
   uint8_t* recs;         // workspace records
   float scale;
@@ -31,6 +32,15 @@ struct Params {
   int B, T, HQK, HV, K, V, N;
   int NT;                // fixed length: chunks per sequence
   int64_t max_chunks;    // workspace capacity in chunks (per value head)
+  // Segmented scan: each sequence is cut into segments of seg_L chunks that are
+  // scanned in parallel (kda_scan.hip).
+  bool seg_path;         // the segmented scan runs (kda_scan.hip), else the serial one (kda_inter.hip)
+  int seg_L;             // chunks per segment
+  int seg_S;             // fixed length: segments per sequence
+  int64_t max_segs;      // capacity of the segment buffers (segments over all sequences)
+  int32_t* segtab;       // varlen: seg_base[N+1] in the workspace header, else nullptr
+  float* bbuf;           // [max_segs, HV, K, V] fp32 segment end states, or nullptr (one segment)
+  uint16_t* mbuf;        // [max_segs, HV, K, K] bf16 segment transitions, or nullptr
 };
 
 // Reverse state scan of the backward (kda_bwd_dhu).
@@ -54,12 +64,18 @@ struct BwdParams {
 };
 
 // Host launchers (return the hipError_t of the launch).
-// varlen chunk table (chunk_base[N+1], error flag at [N+1]); also zeroes *counter when non-null
+// varlen chunk table (chunk_base[N+1], error flag at [N+1]); also zeroes *counter when
+// non-null, writes seg_base[N+1] (segments of seg_L chunks, at least one per
+// sequence) when segtab is non-null and per-chunk {first row, valid rows} when
+// cinfo is non-null
 hipError_t launch_chunk_table(const int64_t* cu, int N, int T, int64_t max_chunks, int32_t* table,
-                              int32_t* counter, hipStream_t s);
+                              int32_t* counter, int seg_L, int64_t max_segs, int32_t* segtab, int2* cinfo,
+                              hipStream_t s);
+int device_cus();                                               // compute units of the current device
 hipError_t launch_prep(const Params& p, hipStream_t s);          // fixed length: zeroes the counter
 hipError_t launch_intra(const Params& p, hipStream_t s);
 hipError_t launch_inter(const Params& p, hipStream_t s);
+hipError_t launch_scan(const Params& p, hipStream_t s);          // segmented scan (both passes)
 hipError_t launch_bwd_dhu(const BwdParams& p, hipStream_t s);
 hipError_t launch_unpack(const Params& p, uint16_t* qg, uint16_t* w, uint16_t* kg,
                          uint16_t* aqk, uint16_t* tmb, float* alpha, hipStream_t s);

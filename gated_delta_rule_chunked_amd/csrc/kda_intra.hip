@@ -67,7 +67,11 @@ struct ChunkLoc {
 
 // Chunk gc -> (batch row, first row, valid rows).  Returns false when gc is past
 // the last chunk (varlen capacity padding) or the chunk table was rejected.
-__device__ __forceinline__ bool locate_chunk(const Params& p, int64_t gc, ChunkLoc& c) {
+// The varlen table and chunk info come in as read-only, non-aliasing pointers: with
+// a uniform chunk index their loads are scalar loads, which wait on their own
+// counter, never on the vector stores of the records in flight.
+__device__ __forceinline__ bool locate_chunk(const Params& p, const int32_t* __restrict__ tb,
+                                             const int2* __restrict__ cinfo, int64_t gc, ChunkLoc& c) {
   if (p.cu == nullptr) {
     int n = (int)(gc / p.NT);
     if (n >= p.B) return false;
@@ -76,26 +80,25 @@ __device__ __forceinline__ bool locate_chunk(const Params& p, int64_t gc, ChunkL
     c.L = (int)min<int64_t>(BT, p.T - c.row0);
     return c.L > 0;
   }
-  const int32_t* tb = p.table;
   if (tb[p.N + 1] != 0 || gc >= tb[p.N]) return false;
-  int lo = 0, hi = p.N - 1;  // last n with tb[n] <= gc
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (tb[mid] <= gc) lo = mid; else hi = mid - 1;
-  }
+  const int2 ci = cinfo[gc];   // first row and valid rows, written by the chunk table kernel
   c.b = 0;
-  c.row0 = p.cu[lo] + (gc - tb[lo]) * BT;
-  c.L = (int)min<int64_t>(BT, p.cu[lo + 1] - c.row0);
+  c.row0 = ci.x;
+  c.L = ci.y;
   return c.L > 0;
 }
 
 // ----------------------------------------------------------- chunk table
 // One workgroup: chunk_base[n] = sum_{m<n} ceil(len_m / 64) (the tile_base of the
 // FlashKDA walkthrough's sequence-information section), chunk_base[N] = total,
-// and an error flag at [N+1] if cu_seqlens is not 0 = cu[0] <= ... <= cu[N] = T.
+// and an error flag at [N+1] if cu_seqlens is not 0 = cu[0] <= ... <= cu[N] = T;
+// optionally the segment table and, per chunk, its first row and valid rows (so the
+// intra stage finds a chunk with one load instead of a search over the table).
 __global__ __launch_bounds__(256) void chunk_table_kernel(const int64_t* cu, int N, int T, int64_t max_chunks,
-                                                           int32_t* table, int32_t* counter) {
+                                                           int32_t* table, int32_t* counter, int seg_L,
+                                                           int64_t max_segs, int32_t* segtab, int2* cinfo) {
   __shared__ int32_t scan[256];
+  __shared__ int32_t sscan[256];
   __shared__ int32_t bad_any;
   const int tid = threadIdx.x;
   if (tid == 0) {
@@ -103,30 +106,45 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int64_t* cu, int
     if (counter) *counter = 0;   // work counter of the intra stage
   }
   __syncthreads();
-  int32_t running = 0;
+  int32_t running = 0, srunning = 0;
   for (int base = 0; base < N; base += 256) {
     const int n = base + tid;
-    int32_t cnt = 0;
+    int32_t cnt = 0, scnt = 0;
     if (n < N) {
       const int64_t a = cu[n], e = cu[n + 1];
       if (a < 0 || e < a || e > T) atomicOr(&bad_any, 1);
       else cnt = (int32_t)((e - a + BT - 1) / BT);
+      scnt = cnt > seg_L ? (cnt + seg_L - 1) / seg_L : 1;   // segments, at least one per sequence
     }
     scan[tid] = cnt;
+    sscan[tid] = scnt;
     __syncthreads();
     for (int off = 1; off < 256; off <<= 1) {
-      int32_t add = tid >= off ? scan[tid - off] : 0;
+      const int32_t add = tid >= off ? scan[tid - off] : 0;
+      const int32_t sadd = tid >= off ? sscan[tid - off] : 0;
       __syncthreads();
       scan[tid] += add;
+      sscan[tid] += sadd;
       __syncthreads();
     }
-    if (n < N) table[n] = running + scan[tid] - cnt;
+    if (n < N) {
+      const int32_t first = running + scan[tid] - cnt;
+      table[n] = first;
+      if (segtab) segtab[n] = srunning + sscan[tid] - scnt;
+      if (cinfo) {   // per chunk: first row, valid rows (a rejected table is never read)
+        const int32_t a0 = (int32_t)cu[n], len = (int32_t)(cu[n + 1] - cu[n]);
+        for (int j = 0; j < cnt && first + j < max_chunks; ++j)
+          cinfo[first + j] = make_int2(a0 + BT * j, min(BT, len - BT * j));
+      }
+    }
     running += scan[255];
+    srunning += sscan[255];
     __syncthreads();
   }
   if (tid == 0) {
     table[N] = running;
-    table[N + 1] = (bad_any || running > max_chunks) ? 1 : 0;
+    if (segtab) segtab[N] = srunning;
+    table[N + 1] = (bad_any || running > max_chunks || (segtab && srunning > max_segs)) ? 1 : 0;
   }
 }
 
@@ -141,7 +159,9 @@ __global__ void prep_kernel(Params p) {
 #define KDA_INTRA_OCC 2   // workgroups per CU the register budget is sized for
 #endif
 template <int K>
-__global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p, int n_items) {
+__global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p, int n_items,
+                                                                         const int32_t* __restrict__ tbl,
+                                                                         const int2* __restrict__ cinfo) {
   using SM = IntraSmem<K>;
   using R = Rec<K>;
   constexpr int S = SM::S;
@@ -167,15 +187,38 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
   // while the current one is computed (phases 2-3).  lane dims for step s, element e:
   // d = 32s + pidx(g, e)
   __shared__ int s_next;
+  __shared__ long long s_nrow;   // first token row of s_next's chunk (batch row folded in)
+  __shared__ int s_nlen;         // its valid rows; 0 when there is nothing to do
   uint4 nq[S], nk[S], ng[S];
   uint32_t nb = 0;   // raw bf16 bits: converting here would wait for the loads
-  // one input of the next item: 0 = q, 1 = k, 2 = g and beta
-  auto fetch_part = [&](int it, int part) {
+  // Location of item `it`: first token row and valid rows (0 past the last item, for
+  // varlen capacity padding and for a rejected table).
+  auto locate_item = [&](int it, int64_t& row, int& len) {
+    it = __builtin_amdgcn_readfirstlane(it);
     ChunkLoc c;
-    const bool ok = it < n_items && locate_chunk(p, it / p.HV, c);
+    const bool ok = it < n_items && locate_chunk(p, tbl, cinfo, it / p.HV, c);
+    row = ok ? (int64_t)c.b * p.T + c.row0 : 0;
+    len = ok ? c.L : 0;
+  };
+  // Next ticket and its location, by thread 0.  Varlen locations are table loads;
+  // made here, right after the ticket atomic (whose result is awaited anyway), they
+  // never make the item loads wait for the record stores still in flight.
+  auto draw_ticket = [&]() {
+    if (tid == 0) {
+      const int t = (int)gridDim.x + atomicAdd(p.counter, 1);
+      int64_t row;
+      int len;
+      locate_item(t, row, len);
+      s_next = t;
+      s_nrow = row;
+      s_nlen = len;
+    }
+  };
+  // one input of item `it` at (row, len): 0 = q, 1 = k, 2 = g and beta
+  auto fetch_part = [&](int it, int64_t row0, int len, int part) {
     const int h = it % p.HV;
-    const bool valid = ok && i < c.L;
-    const int64_t tk = ok ? (int64_t)c.b * p.T + c.row0 + i : 0;
+    const bool valid = i < len;
+    const int64_t tk = valid ? row0 + i : 0;
     const uint16_t* row = part == 0 ? p.q + (tk * p.HQK + h / (p.HV / p.HQK)) * K
                         : part == 1 ? p.k + (tk * p.HQK + h / (p.HV / p.HQK)) * K
                                     : p.g + (tk * p.HV + h) * K;
@@ -197,21 +240,28 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
       if (valid) nb = p.beta[tk * p.HV + h];
     }
   };
-  auto fetch = [&](int it) {
-    fetch_part(it, 0);
-    fetch_part(it, 1);
-    fetch_part(it, 2);
+  auto fetch = [&](int it, int64_t row0, int len) {
+    fetch_part(it, row0, len, 0);
+    fetch_part(it, row0, len, 1);
+    fetch_part(it, row0, len, 2);
   };
   int item = xcd_remap(blockIdx.x, gridDim.x);
-  fetch(item);
-  if (tid == 0) s_next = (int)gridDim.x + atomicAdd(p.counter, 1);
+  int cur_len;   // valid rows of `item`
+  {
+    int64_t row;
+    locate_item(item, row, cur_len);
+    fetch(item, row, cur_len);
+  }
+  draw_ticket();
   __syncthreads();
   while (item < n_items) {
-  const int next = s_next;   // written before the last barrier; rewritten only after B9
+  // written before the last barrier; rewritten only after B9
+  const int next = __builtin_amdgcn_readfirstlane(s_next);
+  const int64_t next_row = s_nrow;
+  const int next_len = __builtin_amdgcn_readfirstlane(s_nlen);
   const int hv = item % p.HV;
   const int64_t gc = item / p.HV;
-  ChunkLoc cl;
-  const bool live = locate_chunk(p, gc, cl);   // uniform over the workgroup
+  const bool live = cur_len > 0;   // uniform over the workgroup
   uint4 uqs[S], uks[S];   // q, k kept packed (bf16) until used
   float gl[S][8];
   float bt;
@@ -225,11 +275,12 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
   if (p.flags & FLAG_BETA_LOGITS)   // FlashKDA's fused sigmoid: 1 / (1 + e^-x), exact 0 and 1 at -inf, +inf
     bt = 1.f / (1.f + __builtin_amdgcn_exp2f(-LOG2E * bt));
   if (!live) {   // varlen capacity padding or rejected table: nothing to write
-    fetch(next);
+    fetch(next, next_row, next_len);
     __syncthreads();   // every thread has read s_next
-    if (tid == 0) s_next = (int)gridDim.x + atomicAdd(p.counter, 1);
+    draw_ticket();
     __syncthreads();
     item = next;
+    cur_len = next_len;
     continue;
   }
   uint8_t* rec = p.recs + rec_index(hv, gc, p.max_chunks) * (int64_t)R::BYTES;
@@ -332,7 +383,7 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
   // The next item's inputs load in three parts spread over phases 2-3 (g here, q
   // after B6, k after B7): issued at once they waited about 6k cycles per item
   // for queue space behind this item's record stores.
-  fetch_part(next, 2);   // g and beta of the next item
+  fetch_part(next, next_row, next_len, 2);   // g and beta of the next item
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const uint32_t wd[4] = {KD[s].x, KD[s].y, KD[s].z, KD[s].w};
@@ -393,7 +444,7 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
   for (int J = 0; J < 4; ++J)
     *reinterpret_cast<float4*>(sAkk + i * SM::AS + 16 * J + 4 * g) = make_float4(vk[J][0], vk[J][1], vk[J][2], vk[J][3]);
   __syncthreads();  // B6: Akk and (k exp(Gam))^T complete
-  fetch_part(next, 0);   // q of the next item
+  fetch_part(next, next_row, next_len, 0);   // q of the next item
 
   // ---- phase 3: Tm = (I + Akk)^-1 ------------------------------------------------
   // 3a: inverse of the unit lower diagonal block I + N (N strictly lower, so
@@ -432,7 +483,7 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
     for (int e = 0; e < 4; ++e) Aw[(4 * g + e) * SM::AS + r] = D[e];
   }
   __syncthreads();  // B7: diagonal blocks hold D_I
-  fetch_part(next, 1);   // k of the next item
+  fetch_part(next, next_row, next_len, 1);   // k of the next item
 
   // 3b: block column J = I below the diagonal:
   //     Inv_MJ = -D_M sum_{J<=P<M} A_MP Inv_PJ   (Inv_JJ = D_J),
@@ -513,9 +564,10 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
     }
     store_stream(rec + R::WN + ((I * S + s) * 64 + ln) * 16, pack_pair(-acc[0], -acc[1]));
   }
-  if (tid == 0) s_next = (int)gridDim.x + atomicAdd(p.counter, 1);   // ticket for the item after next
+  draw_ticket();     // ticket (and location) for the item after next
   __syncthreads();  // B10: phase-4 reads of Tm, beta and (k exp(Gam))^T are done; s_next visible
   item = next;
+  cur_len = next_len;
   }
 }
 
@@ -532,7 +584,7 @@ __global__ __launch_bounds__(NTHREADS) void unpack_kernel(Params p, int n_items,
   const int hv = item % p.HV;
   const int64_t gc = item / p.HV;
   ChunkLoc cl;
-  if (!locate_chunk(p, gc, cl)) return;
+  if (!locate_chunk(p, p.table, p.cinfo, gc, cl)) return;
   const uint8_t* rec = p.recs + rec_index(hv, gc, p.max_chunks) * (int64_t)R::BYTES;
   const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, r = ln & 15, g = ln >> 4;
   auto tokrow = [&](int t) { return ((int64_t)cl.b * p.T + cl.row0 + t) * p.HV + hv; };
@@ -585,13 +637,15 @@ __global__ __launch_bounds__(NTHREADS) void unpack_kernel(Params p, int n_items,
 static int padded8(int64_t n) { return (int)((n + 7) / 8 * 8); }
 
 hipError_t launch_chunk_table(const int64_t* cu, int N, int T, int64_t max_chunks, int32_t* table,
-                              int32_t* counter, hipStream_t s) {
-  hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, s, cu, N, T, max_chunks, table, counter);
+                              int32_t* counter, int seg_L, int64_t max_segs, int32_t* segtab, int2* cinfo,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, s, cu, N, T, max_chunks, table, counter,
+                     seg_L, max_segs, segtab, cinfo);
   return hipGetLastError();
 }
 
 // Compute units of the current device (cached per device id).
-static int device_cus() {
+int device_cus() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -613,8 +667,8 @@ hipError_t launch_intra(const Params& p, hipStream_t s) {
   if (items == 0) return hipSuccess;
   // persistent grid: KDA_INTRA_OCC resident workgroups per CU, each looping over items
   const int grid = padded8(std::min<int64_t>(items, (int64_t)device_cus() * KDA_INTRA_OCC));
-  if (p.K == 128) hipLaunchKernelGGL(intra_kernel<128>, dim3(grid), dim3(NTHREADS), 0, s, p, (int)items);
-  else hipLaunchKernelGGL(intra_kernel<64>, dim3(grid), dim3(NTHREADS), 0, s, p, (int)items);
+  if (p.K == 128) hipLaunchKernelGGL(intra_kernel<128>, dim3(grid), dim3(NTHREADS), 0, s, p, (int)items, p.table, p.cinfo);
+  else hipLaunchKernelGGL(intra_kernel<64>, dim3(grid), dim3(NTHREADS), 0, s, p, (int)items, p.table, p.cinfo);
   return hipGetLastError();
 }
 

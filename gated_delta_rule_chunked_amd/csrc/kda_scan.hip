@@ -1,0 +1,459 @@
+// kda_scan.hip -- segmented inter-chunk state scan of the KDA chunked forward (gfx950).
+//
+// Per chunk, following the kernel-fun fwd_state module docstring (and FlashKDA's
+// phases 3-6), with h the fp32 state [K, V] of one sequence and value head:
+//   u   = TmB v                      (TmB = Tm diag(beta))
+//   v'  = u - w h
+//   o   = qg h + Aqk v'              (scale folded into qg and Aqk)
+//   h  <- diag(exp2 G) h + kg^T v'
+//
+// Work decomposition.  A workgroup covers 64 value columns (four 16-column column
+// waves) of one segment of seg_L consecutive chunks, and stages each chunk's record
+// once for all four: per useful column, a CU streams a quarter of the record bytes
+// of a 16-column workgroup, which is what bounds a scan workgroup (its L1 sits at
+// the limit of outstanding misses).  Segments restore the parallelism the wider
+// tiles take away.  Over one segment the scan is affine in its start state,
+//     h_end = M h_start + b,     M = prod_c (diag(exp2 G_c) - kg_c^T w_c),
+// so two passes give the exact result:
+//   * the state pass computes, for every segment but a sequence's last, b (the end
+//     state from h0 for the first segment, from zero otherwise) and, for every
+//     segment but the first and the last, M -- by scanning the columns of the
+//     identity with v = 0 (u = 0);
+//   * the full pass starts segment s from h_s, with h_1 = b_0 and
+//     h_s = M_{s-1} h_{s-1} + b_{s-1} formed in its prologue, and writes o (and the
+//     final state after the last segment).
+// b is kept in fp32, M in bf16 (it multiplies a bf16 copy of h on MFMA, as w does
+// within a chunk).
+//
+// Eight waves per workgroup, one barrier per chunk:
+//   waves 0-3 (column waves): wave c holds h for columns 16c..16c+15 of the group
+//     in the C layout of 16x16 MFMA tiles and runs the whole chunk in registers:
+//     u, v', the update of h and (full pass) o^T = h^T qg^T + v'^T Aqk^T, whose C
+//     layout gives each lane four adjacent columns of one token (8-byte stores).
+//     Operands come from the staged record; v^T fragments by transpose reads of the
+//     row-major v tile.
+//   waves 4-7 (loader waves): keep three chunks of records in flight in a register
+//     ring (1 KiB steps of the record, steps lw, lw+4, ...) together with the v
+//     tile of column wave lw, and copy chunk c+1 into the free slot of a two-slot
+//     LDS ring during chunk c.
+
+#include "kda_device.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+
+constexpr int SCAN_THREADS = 512;
+constexpr int SCAN_RING = 3;            // chunks in flight per loader wave
+enum ScanMode { SCAN_FULL = 0, SCAN_B = 1, SCAN_M = 2 };
+
+template <int K, int MODE>
+struct ScanSmem {
+  using R = Rec<K>;
+  // the full pass copies whole records, the state pass only their state part
+  static constexpr int NSTEP = ((MODE == SCAN_FULL ? R::BYTES : R::STATE_BYTES) + 1023) / 1024;
+  static constexpr int NLD = (NSTEP + 3) / 4;        // steps per loader wave (the last ones repeat)
+  static constexpr int SLOT = NSTEP * 1024;
+  static constexpr int VT = 2 * SLOT;                // v tiles: [2 slots][4 column waves][64][16] bf16
+  static constexpr int VT_BYTES = BT * BV * 2;
+  static constexpr int BYTES = VT + (MODE == SCAN_M ? 0 : 2 * 4 * VT_BYTES);
+  static_assert(BYTES <= 160 * 1024, "fits the LDS of one CU");
+};
+
+// One segment of one sequence.
+struct SegLoc {
+  int n, s, nseg;       // sequence, segment within it, its segment count
+  int64_t sigma0;       // index of the sequence's first segment
+  int b;                // batch row
+  int64_t bos;          // first row of the sequence within the batch row
+  int len;              // tokens of the sequence
+  int64_t cbase;        // chunk index of the sequence's first chunk
+  int c0, ncs;          // first chunk of the segment (within the sequence), chunks in it
+};
+
+// Segment sigma -> location.  Returns false when sigma is past the last segment.
+__device__ __forceinline__ bool locate_segment(const Params& p, int64_t sigma, SegLoc& sl) {
+  if (p.cu == nullptr) {
+    const int64_t n = sigma / p.seg_S;
+    if (n >= p.B) return false;
+    sl.n = (int)n;
+    sl.s = (int)(sigma - n * p.seg_S);
+    sl.nseg = p.seg_S;
+    sl.sigma0 = n * p.seg_S;
+    sl.b = (int)n;
+    sl.bos = 0;
+    sl.len = p.T;
+    sl.cbase = n * p.NT;
+  } else {
+    if (sigma >= p.segtab[p.N]) return false;
+    int lo = 0, hi = p.N;                      // segtab[lo] <= sigma < segtab[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.segtab[mid] <= sigma) lo = mid;
+      else hi = mid;
+    }
+    sl.n = lo;
+    sl.sigma0 = p.segtab[lo];
+    sl.s = (int)(sigma - sl.sigma0);
+    sl.nseg = p.segtab[lo + 1] - p.segtab[lo];
+    sl.b = 0;
+    sl.bos = p.cu[lo];
+    sl.len = (int)(p.cu[lo + 1] - p.cu[lo]);
+    sl.cbase = p.table[lo];
+  }
+  const int nc = (sl.len + BT - 1) / BT;
+  sl.c0 = sl.s * p.seg_L;
+  sl.ncs = max(0, min(p.seg_L, nc - sl.c0));
+  return true;
+}
+
+// The chunks of one segment for one value head and 64-column group (`grp`: value
+// columns 64 grp.., or key columns 64 grp.. of M in SCAN_M), with `ntiles` active
+// column waves.
+template <int K, int MODE>
+__device__ __forceinline__ void scan_body(const Params& p, uint8_t* smem, const SegLoc& sl, int hv, int grp,
+                                          int ntiles, int64_t sigma) {
+  using SM = ScanSmem<K, MODE>;
+  using R = Rec<K>;
+  constexpr int S = K / 32, ND = K / 16;
+  const int tid = threadIdx.x, ln = tid & 63, r = ln & 15, g = ln >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool state_bf16 = p.flags & FLAG_STATE_BF16;
+  const int ncs = sl.ncs;
+  const int nphase = (ncs + SCAN_RING - 1) / SCAN_RING * SCAN_RING;
+  const int64_t row0 = (int64_t)sl.b * p.T + sl.bos;        // first token row of the sequence
+  auto chunk_of = [&](int ph) { return sl.c0 + min(ph, ncs - 1); };   // tail phases re-read the last chunk
+
+  if (wave >= 4) {
+    // ============================ loader waves ============================
+    constexpr int NLD = SM::NLD;
+    const int lw = wave - 4;
+    if (ncs == 0) {
+      barrier_lds();  // S0
+      return;
+    }
+    const int vcol = min(grp * 64 + BV * lw, p.V - BV);        // v tile of column wave lw (clamped)
+    auto fetch = [&](int ph, u32x4* dst, uint4& v0, uint4& v1) {
+      const int c = chunk_of(ph);
+      const uint8_t* rec = p.recs + rec_index(hv, sl.cbase + c, p.max_chunks) * (int64_t)R::BYTES + ln * 16;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) dst[i] = *reinterpret_cast<const u32x4*>(rec + min(4 * i + lw, SM::NSTEP - 1) * 1024);
+      if (MODE != SCAN_M) {
+        const int64_t t = row0 + min(c * BT + ln, sl.len - 1);
+        const uint16_t* vr = p.v + (t * p.HV + hv) * p.V + vcol;
+        v0 = *reinterpret_cast<const uint4*>(vr);
+        v1 = *reinterpret_cast<const uint4*>(vr + 8);
+      }
+    };
+    auto put = [&](int ph, const u32x4* src, const uint4& v0, const uint4& v1) {
+      uint8_t* slot = smem + (ph & 1) * SM::SLOT + ln * 16;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) *reinterpret_cast<u32x4*>(slot + min(4 * i + lw, SM::NSTEP - 1) * 1024) = src[i];
+      if (MODE != SCAN_M) {
+        const bool ok = chunk_of(ph) * BT + ln < sl.len;      // rows past the sequence are zero
+        uint8_t* vt = smem + SM::VT + ((ph & 1) * 4 + lw) * SM::VT_BYTES + ln * 32;
+        *reinterpret_cast<uint4*>(vt) = ok ? v0 : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(vt + 16) = ok ? v1 : make_uint4(0, 0, 0, 0);
+      }
+    };
+    u32x4 ra[NLD], rb[NLD], rc[NLD];
+    uint4 va0, va1, vb0, vb1, vc0, vc1;
+    fetch(0, ra, va0, va1);
+    fetch(1, rb, vb0, vb1);
+    fetch(2, rc, vc0, vc1);
+    put(0, ra, va0, va1);
+    barrier_lds();  // S0: chunk 0 of the segment in slot 0
+    static_assert(SCAN_RING == 3, "the ring turn below is written out for three slots");
+    for (int t0 = 0; t0 < nphase; t0 += SCAN_RING) {
+      fetch(t0 + 3, ra, va0, va1);
+      __builtin_amdgcn_sched_barrier(0);   // loads issue before the LDS writes
+      put(t0 + 1, rb, vb0, vb1);
+      barrier_lds();
+      fetch(t0 + 4, rb, vb0, vb1);
+      __builtin_amdgcn_sched_barrier(0);
+      put(t0 + 2, rc, vc0, vc1);
+      barrier_lds();
+      fetch(t0 + 5, rc, vc0, vc1);
+      __builtin_amdgcn_sched_barrier(0);
+      put(t0 + 3, ra, va0, va1);
+      barrier_lds();
+    }
+    return;
+  }
+
+  // ============================ column waves ============================
+  const int cw = wave;
+  if (cw >= ntiles) {                         // columns past V: keep the barrier count only
+    for (int ph = 0; ph <= nphase; ++ph) barrier_lds();
+    return;
+  }
+  const int col = grp * 64 + BV * cw + r;     // this lane's column (of V, or of K in SCAN_M)
+  // h tile md: lane holds h[16md + 4g + rr][col], rr = 0..3
+  f32x4 h[ND];
+  if (MODE == SCAN_M) {
+#pragma unroll
+    for (int md = 0; md < ND; ++md)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) h[md][rr] = (16 * md + 4 * g + rr == col) ? 1.f : 0.f;
+  } else if (sl.s == 0 || MODE == SCAN_B) {
+    const bool from_h0 = sl.s == 0 && p.h0 != nullptr;
+#pragma unroll
+    for (int md = 0; md < ND; ++md)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d = 16 * md + 4 * g + rr;
+        h[md][rr] = from_h0 ? load_state(state_bf16, p.h0, (((int64_t)sl.n * p.HV + hv) * K + d) * p.V + col) : 0.f;
+      }
+  } else {
+    // full pass, s >= 1: h_1 = b_0, h_{s'+1} = M_{s'} h_{s'} + b_{s'}
+    auto load_b = [&](int64_t sig, f32x4* x) {
+      const float* bb = p.bbuf + ((sig * p.HV + hv) * K) * (int64_t)p.V + col;
+#pragma unroll
+      for (int md = 0; md < ND; ++md)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) x[md][rr] = bb[(int64_t)(16 * md + 4 * g + rr) * p.V];
+    };
+    load_b(sl.sigma0, h);
+    for (int s2 = 1; s2 < sl.s; ++s2) {
+      uint2 hb[ND];
+#pragma unroll
+      for (int md = 0; md < ND; ++md) hb[md] = pack4(h[md]);
+      f32x4 hn[ND];
+      load_b(sl.sigma0 + s2, hn);
+      const uint16_t* M = p.mbuf + ((sl.sigma0 + s2) * p.HV + hv) * (int64_t)K * K + r * K + 4 * g;
+#pragma unroll
+      for (int md = 0; md < ND; ++md)
+#pragma unroll
+        for (int s3 = 0; s3 < S; ++s3) {
+          const uint16_t* a = M + 16 * md * K + 32 * s3;
+          hn[md] = mfma16x32(cat(*reinterpret_cast<const uint2*>(a), *reinterpret_cast<const uint2*>(a + 16)),
+                             cat(hb[2 * s3], hb[2 * s3 + 1]), hn[md]);
+        }
+#pragma unroll
+      for (int md = 0; md < ND; ++md) h[md] = hn[md];
+    }
+  }
+  // per-lane parts of the LDS addresses of the v tile's transpose reads
+  const int tr16 = ((4 * (ln >> 4) + ((ln >> 2) & 3)) * BV + 4 * (ln & 3)) * 2;
+  // o: this lane's columns in the sequence's first row, and the row stride
+  const int orow = p.HV * p.V;
+  uint16_t* const obase = p.o + (row0 * p.HV + hv) * p.V + grp * 64 + BV * cw + 4 * g;
+  barrier_lds();  // S0
+  for (int ph = 0; ph < nphase; ++ph) {
+    if (ph < ncs) {
+      const int c = sl.c0 + ph;
+      if (MODE == SCAN_FULL && p.hc) {   // the state before this chunk
+        // the row stride is re-made opaque every chunk, so the 32 row offsets stay
+        // transient scalars instead of being hoisted as live 64-bit addresses
+        int sv = p.V;
+        asm volatile("" : "+s"(sv));
+        const int64_t base = (((sl.cbase + c) * p.HV + hv) * K + 4 * g) * (int64_t)sv + col;
+        if (state_bf16) {
+          uint16_t* dst = static_cast<uint16_t*>(p.hc) + base;
+#pragma unroll
+          for (int md = 0; md < ND; ++md)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) dst[(int64_t)(16 * md + rr) * sv] = f2bf(h[md][rr]);
+        } else {
+          float* dst = static_cast<float*>(p.hc) + base;
+#pragma unroll
+          for (int md = 0; md < ND; ++md)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) dst[(int64_t)(16 * md + rr) * sv] = h[md][rr];
+        }
+      }
+      const uint8_t* st = smem + (ph & 1) * SM::SLOT;
+      // batch 1: v^T fragments, TmB, decay, -w (in the order they are consumed)
+      bf16x8 vb0, vb1;
+      uint4 tm[6];
+      if (MODE != SCAN_M) {
+        const uint8_t* vt = smem + SM::VT + ((ph & 1) * 4 + cw) * SM::VT_BYTES + tr16;
+        vb0 = cat(lds_tr8(vt), lds_tr8(vt + 16 * BV * 2));
+        vb1 = cat(lds_tr8(vt + 32 * BV * 2), lds_tr8(vt + 48 * BV * 2));
+#pragma unroll
+        for (int f = 0; f < 6; ++f) tm[f] = lds16(st + R::TMB + (f * 64 + ln) * 16);
+      }
+      float4 al[ND];
+      uint4 wn[4 * S];
+#pragma unroll
+      for (int md = 0; md < ND; ++md) al[md] = *reinterpret_cast<const float4*>(st + R::ALPHA + (16 * md + 4 * g) * 4);
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) wn[s * 4 + mb] = lds16(st + R::WN + ((mb * S + s) * 64 + ln) * 16);
+      __builtin_amdgcn_sched_barrier(0);
+      // u = TmB v, row blocks mb = 0..3 (lower triangular: 1 or 2 32-steps); zero in SCAN_M
+      f32x4 acc[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        if (MODE != SCAN_M) {
+          acc[mb] = mfma16x32(as_frag(tm[tri_frag(mb, 0)]), vb0, f32x4{0.f, 0.f, 0.f, 0.f});
+          if (mb >= 2) acc[mb] = mfma16x32(as_frag(tm[tri_frag(mb, 1)]), vb1, acc[mb]);
+        } else {
+          acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      // h as the bf16 B operand (tiles 2s, 2s+1 form the P-order fragment of step s);
+      // then h <- diag(alpha) h
+      uint2 hb[ND];
+#pragma unroll
+      for (int md = 0; md < ND; ++md) {
+        hb[md] = pack4(h[md]);
+        h[md][0] *= al[md].x;
+        h[md][1] *= al[md].y;
+        h[md][2] *= al[md].z;
+        h[md][3] *= al[md].w;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // batch 2: kg^T
+      uint4 kg[2 * ND];
+#pragma unroll
+      for (int i = 0; i < 2 * ND; ++i) kg[i] = lds16(st + R::KGT + (i * 64 + ln) * 16);
+      __builtin_amdgcn_sched_barrier(0);
+      // v' = u + (-w) h
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const bf16x8 hbs = cat(hb[2 * s], hb[2 * s + 1]);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) acc[mb] = mfma16x32(as_frag(wn[s * 4 + mb]), hbs, acc[mb]);
+      }
+      uint2 vp[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) vp[mb] = pack4(acc[mb]);
+      // h <- diag(alpha) h + kg^T v'   (v' tiles (2s2, 2s2+1) = P-order token step s2)
+      const bf16x8 vp0 = cat(vp[0], vp[1]), vp1 = cat(vp[2], vp[3]);
+#pragma unroll
+      for (int md = 0; md < ND; ++md) {
+        h[md] = mfma16x32(as_frag(kg[2 * md]), vp0, h[md]);
+        h[md] = mfma16x32(as_frag(kg[2 * md + 1]), vp1, h[md]);
+      }
+      if (MODE == SCAN_FULL) {
+        // o^T = h^T qg^T + v'^T Aqk^T per 16-token row block w: the P-order fragments
+        // of h (before the update) and v' as A operands, the record's qg / Aqk
+        // fragments as B operands; lane (g, r) gets token 16w + r, columns 4g..4g+3.
+        // All four blocks first, the guarded stores after, so that no branch splits
+        // the operand reads from the products.
+        __builtin_amdgcn_sched_barrier(0);
+        uint2 ov[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint4 qg[S], aq[2];
+#pragma unroll
+          for (int s = 0; s < S; ++s) qg[s] = lds16(st + R::QG + ((w * S + s) * 64 + ln) * 16);
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+            aq[s2] = lds16(st + R::AQK + (tri_frag(w, min(s2, tri_steps(w) - 1)) * 64 + ln) * 16);
+          f32x4 oacc = f32x4{0.f, 0.f, 0.f, 0.f}, oacc2 = oacc;
+#pragma unroll
+          for (int s = 0; s < S; s += 2) {
+            oacc = mfma16x32(cat(hb[2 * s], hb[2 * s + 1]), as_frag(qg[s]), oacc);
+            oacc2 = mfma16x32(cat(hb[2 * s + 2], hb[2 * s + 3]), as_frag(qg[s + 1]), oacc2);
+          }
+          oacc = mfma16x32(vp0, as_frag(aq[0]), oacc);
+          if (tri_steps(w) > 1) oacc2 = mfma16x32(vp1, as_frag(aq[1]), oacc2);
+          ov[w] = pack4(oacc + oacc2);
+        }
+        uint16_t* oc = obase + (int64_t)(c * BT) * orow;      // this chunk's first row
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          if (c * BT + 16 * w + r < sl.len) *reinterpret_cast<uint2*>(oc + (16 * w + r) * orow) = ov[w];
+      }
+    }
+    barrier_lds();
+  }
+  // the segment's end state
+  if (MODE == SCAN_B) {
+    float* bb = p.bbuf + ((sigma * p.HV + hv) * K) * (int64_t)p.V + col;
+#pragma unroll
+    for (int md = 0; md < ND; ++md)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) bb[(int64_t)(16 * md + 4 * g + rr) * p.V] = h[md][rr];
+  } else if (MODE == SCAN_M) {
+    uint16_t* mm = p.mbuf + (sigma * p.HV + hv) * (int64_t)K * K + col;
+#pragma unroll
+    for (int md = 0; md < ND; ++md)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) mm[(16 * md + 4 * g + rr) * K] = f2bf(h[md][rr]);
+  } else if (p.ht && sl.s == sl.nseg - 1) {
+#pragma unroll
+    for (int md = 0; md < ND; ++md)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d = 16 * md + 4 * g + rr;
+        store_state(state_bf16, p.ht, (((int64_t)sl.n * p.HV + hv) * K + d) * p.V + col, h[md][rr]);
+      }
+  }
+}
+
+// State pass: item = ((sigma * HV + hv) * (NCG + K/64) + j); j < NCG is the b task of
+// value-column group j, j >= NCG the M task of key-column group j - NCG.
+template <int K>
+__global__ __launch_bounds__(SCAN_THREADS, 1) void scan_state_kernel(Params p, int n_items) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[ScanSmem<K, SCAN_B>::BYTES];
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  if (item >= n_items) return;
+  if (p.cu != nullptr && p.table[p.N + 1] != 0) return;   // rejected cu_seqlens: the full pass reports it
+  const int NCG = (p.V + 63) / 64, NJ = NCG + K / 64;
+  const int j = item % NJ;
+  const int hv = (item / NJ) % p.HV;
+  const int64_t sigma = item / (NJ * p.HV);
+  SegLoc sl;
+  if (!locate_segment(p, sigma, sl)) return;
+  if (j < NCG) {
+    if (sl.s >= sl.nseg - 1) return;                  // the last segment's end state is not needed
+    scan_body<K, SCAN_B>(p, smem, sl, hv, j, min(4, (p.V - 64 * j) / BV), sigma);
+  } else {
+    if (sl.s == 0 || sl.s >= sl.nseg - 1) return;     // M is needed between inner segments only
+    scan_body<K, SCAN_M>(p, smem, sl, hv, j - NCG, 4, sigma);
+  }
+}
+
+// Full pass: item = (sigma * HV + hv) * NCG + cg.
+template <int K>
+__global__ __launch_bounds__(SCAN_THREADS, 1) void scan_full_kernel(Params p, int n_items) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[ScanSmem<K, SCAN_FULL>::BYTES];
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  if (item >= n_items) return;
+  const int tid = threadIdx.x;
+  if (p.cu != nullptr && p.table[p.N + 1] != 0) {
+    // rejected cu_seqlens: poison all of o and ht, grid-strided
+    const int64_t total = (int64_t)p.B * p.T * p.HV * p.V;
+    for (int64_t idx = (int64_t)item * SCAN_THREADS + tid; idx < total; idx += (int64_t)n_items * SCAN_THREADS)
+      p.o[idx] = 0x7fc0;
+    if (p.ht) {
+      const int64_t nh = (int64_t)p.N * p.HV * K * p.V;
+      for (int64_t idx = (int64_t)item * SCAN_THREADS + tid; idx < nh; idx += (int64_t)n_items * SCAN_THREADS)
+        store_state(p.flags & FLAG_STATE_BF16, p.ht, idx, __builtin_nanf(""));
+    }
+    return;
+  }
+  const int NCG = (p.V + 63) / 64;
+  const int cg = item % NCG;
+  const int hv = (item / NCG) % p.HV;
+  const int64_t sigma = item / (NCG * p.HV);
+  SegLoc sl;
+  if (!locate_segment(p, sigma, sl)) return;
+  scan_body<K, SCAN_FULL>(p, smem, sl, hv, cg, min(4, (p.V - 64 * cg) / BV), sigma);
+}
+
+template <int K>
+static hipError_t launch_scan_k(const Params& p, hipStream_t s) {
+  const int64_t NCG = (p.V + 63) / 64;
+  if (p.bbuf != nullptr) {
+    const int64_t items = p.max_segs * p.HV * (NCG + K / 64);
+    hipLaunchKernelGGL((scan_state_kernel<K>), dim3((int)((items + 7) / 8 * 8)), dim3(SCAN_THREADS), 0, s, p,
+                       (int)items);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t items = p.max_segs * p.HV * NCG;
+  hipLaunchKernelGGL((scan_full_kernel<K>), dim3((int)((items + 7) / 8 * 8)), dim3(SCAN_THREADS), 0, s, p,
+                     (int)items);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const Params& p, hipStream_t s) {
+  if (p.max_segs * p.HV == 0) return hipSuccess;
+  return p.K == 128 ? launch_scan_k<128>(p, s) : launch_scan_k<64>(p, s);
+}
+
+}  // namespace kda

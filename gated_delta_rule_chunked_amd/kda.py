@@ -39,6 +39,7 @@ class KdaFwdArgs(ctypes.Structure):
         ("workspace", c_void_p), ("workspace_bytes", c_size_t),
         ("stream", c_void_p),
         ("flags", ctypes.c_uint32), ("hc", c_void_p),
+        ("seg_chunks", c_int32),
     ]
 
 
@@ -100,7 +101,7 @@ def _ptr(t):
 
 
 def make_args(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, o=None, ht=None,
-              workspace=None, stream=None, flags=0, hc=None) -> KdaFwdArgs:
+              workspace=None, stream=None, flags=0, hc=None, seg_chunks=0) -> KdaFwdArgs:
     """Fill ``kda_fwd_args`` from torch tensors (shapes as in the header).
 
     q, k: [B, T, HQK, K] bf16; v: [B, T, HV, V] bf16; g: [B, T, HV, K] bf16;
@@ -136,6 +137,7 @@ def make_args(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, o=None, ht
     a.stream = stream
     a.flags = int(flags)
     a.hc = _ptr(hc)
+    a.seg_chunks = int(seg_chunks)
     return a
 
 
@@ -181,13 +183,15 @@ def num_chunks(T, cu_seqlens=None, B=1):
 
 
 def kda_fwd(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, output_final_state=True,
-            o=None, workspace=None, beta_logits=False, state_dtype=None, output_chunk_states=False):
+            o=None, workspace=None, beta_logits=False, state_dtype=None, output_chunk_states=False,
+            seg_chunks=0):
     """Chunked KDA forward on the current stream.
 
     Returns (o, ht or None), or (o, ht or None, hc) with ``output_chunk_states``:
     hc [C, HV, K, V] is the state before each chunk (see ``num_chunks``).
     ``beta_logits``: beta holds logits and the kernel applies the sigmoid.
     ``state_dtype``: torch.float32 (default) or torch.bfloat16 for h0, ht and hc.
+    ``seg_chunks``: segment length of the state scan in chunks (0: chosen by the library).
     Allocates o, ht, hc and the workspace with torch unless given.
     """
     import torch
@@ -207,7 +211,7 @@ def kda_fwd(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, output_final
     hc = None
     if output_chunk_states:
         hc = torch.empty((num_chunks(T, cu_seqlens, B), HV, K, V), dtype=sdt, device=q.device)
-    args = make_args(q, k, v, g, beta, scale, h0, cu_seqlens, o, ht, flags=flags, hc=hc)
+    args = make_args(q, k, v, g, beta, scale, h0, cu_seqlens, o, ht, flags=flags, hc=hc, seg_chunks=seg_chunks)
     if workspace is None:
         workspace = alloc_workspace(args, q.device)
     args.workspace = workspace.data_ptr()

@@ -105,6 +105,12 @@ typedef struct kda_fwd_args {
    * The chunked backward pass needs these (kernel-fun fwd_state module docstring,
    * which keeps h per chunk for the backward). */
   void* hc;
+  /* Segment length of the state scan in chunks (kda_fwd / kda_fwd_inter and the
+   * workspace size), or 0 to let the library choose.  Each sequence is cut into
+   * segments of this many chunks that are scanned in parallel and joined through
+   * the scan's affine dependence on its start state; results do not depend on
+   * it beyond rounding.  Must be >= 0. */
+  int32_t seg_chunks;
 } kda_fwd_args;
 
 /* Workspace size for these arguments (host only, launches nothing).  Only the

@@ -47,7 +47,8 @@ def test_struct_layout_matches_header():
     assert a.scale.offset == 40 and a.h0.offset == 48 and a.cu_seqlens.offset == 56
     assert a.B.offset == 64 and a.N.offset == 88 and a.o.offset == 96
     assert a.workspace_bytes.offset == 120 and a.stream.offset == 128
-    assert a.flags.offset == 136 and a.hc.offset == 144 and ctypes.sizeof(a) == 152
+    assert a.flags.offset == 136 and a.hc.offset == 144 and a.seg_chunks.offset == 152
+    assert ctypes.sizeof(a) == 160
 
 
 def args(**over):
@@ -70,19 +71,43 @@ def ws(a):
 
 
 def test_workspace_bytes(lib):
-    # fixed length: B * ceil(T/64) chunks per value head, one record per (chunk, head)
-    # plus a 256-byte header (work counter; varlen chunk table)
+    # [header | records | (segmented scan: 1 KiB pad | B | M)]: records are one per
+    # (chunk, value head).  The serial scan is chosen when N x HV x V/16 >= half of
+    # the compute units (256 when no device is seen) or there are fewer than 64
+    # chunks; the segmented scan adds one B (fp32 K x V) and one M (bf16 K x K) per
+    # (segment, value head) when a sequence has more than one segment.
+    KV4, KK2 = 128 * 128 * 4, 128 * 128 * 2
+    # T=8192, H=32, K=V=128: 256 serial workgroups -> serial scan
     st, n = ws(args(B=1, T=8192, HQK=32, HV=32))
     assert st == 0 and n == 256 + 128 * 32 * 61952
     st, n = ws(args(B=2, T=200, HQK=1, HV=1, K=64, V=64, N=2))
     assert st == 0 and n == 256 + 2 * 4 * 37120
-    # varlen: ceil(T/64) + N chunk capacity; the chunk table shares the header
+    # varlen: chunk table (N + 2 int32) and per-chunk info (8 bytes per chunk of the
+    # ceil(T/64) + N capacity) in the header: 16 + 7 x 4 -> 48, + 21 x 8 = 216 -> 256
+    # (5 x 2 x 8 = 80 serial workgroups, 16 chunks: serial scan)
     st, n = ws(args(B=1, T=1000, HQK=1, HV=2, N=5, cu_seqlens=1 << 20))
     assert st == 0 and n == 256 + (16 + 5) * 2 * 61952
+    # N=70: 70 x 2 x 2 = 280 wide workgroups fill the device: one segment per sequence;
+    # header 16 + 72 x 4 + 71 x 4 (segment table) = 588, chunk info from 592: + 86 x 8 = 1280
     st, n = ws(args(B=1, T=1000, HQK=1, HV=2, N=70, cu_seqlens=1 << 20))
-    assert st == 0 and n == 512 + (16 + 70) * 2 * 61952
+    assert st == 0 and n == 1280 + (16 + 70) * 2 * 61952 + 1024
+    # T=16384, H=2: 16 serial workgroups, 256 chunks -> segmented, L = max(8, 256/8) = 32, 8 segments
+    st, n = ws(args(B=1, T=16384, HQK=2, HV=2))
+    assert st == 0 and n == 256 + 256 * 2 * 61952 + 1024 + 8 * 2 * (KV4 + KK2)
+    # forced segment length 32 at T=8192: 4 segments per sequence
+    st, n = ws(args(B=1, T=8192, HQK=32, HV=32, seg_chunks=32))
+    assert st == 0 and n == 256 + 128 * 32 * 61952 + 1024 + 4 * 32 * (KV4 + KK2)
+    # forced, one segment per sequence: no B / M
+    st, n = ws(args(B=1, T=8192, HQK=32, HV=32, seg_chunks=128))
+    assert st == 0 and n == 256 + 128 * 32 * 61952 + 1024
+    # forced varlen: header 16 + 7 x 4 (chunk table, flag) + 6 x 4 (segment table) = 68,
+    # chunk info from 72: + 21 x 8 = 240 -> 256;
+    # up to (16 + 5) // 2 + 5 = 15 segments
+    st, n = ws(args(B=1, T=1000, HQK=1, HV=2, N=5, cu_seqlens=1 << 20, seg_chunks=2))
+    assert st == 0 and n == 256 + (16 + 5) * 2 * 61952 + 1024 + 15 * 2 * (KV4 + KK2)
     st, n = ws(args(T=0))
     assert st == 0 and n == 0
+    assert ws(args(seg_chunks=-1))[0] == K.KDA_ERR_INVALID_ARG
 
 
 ALL = ("kda_fwd", "kda_fwd_intra", "kda_fwd_inter")

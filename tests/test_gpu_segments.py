@@ -1,0 +1,112 @@
+"""Parity of the segmented state scan against the fp64 token recurrence, with the
+segment length forced (kda_fwd_args.seg_chunks) so that every path runs: many
+segments (the prologue chain through M and b), partial 64-column groups, K = 64,
+varlen with empty and one-chunk sequences, h0 entering through the first segment,
+per-chunk states and bf16 states across segment boundaries.  Bar as for the
+forward: max|x - x_ref| / max|x_ref| <= 1e-2 for o, ht (and hc)."""
+import numpy as np
+import pytest
+
+from oracle import chunked, recurrent
+from synth.inputs import make_inputs, round_to_bf16
+
+from _gpu_util import FIELDS, nerr, to_device
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_delta_rule_chunked_amd import load_library
+    load_library()
+
+
+def run(d, t=None, **kw):
+    import torch
+    from gated_delta_rule_chunked_amd import kda_fwd
+    t = t if t is not None else to_device(d)
+    out = kda_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=d["scale"], h0=t["h0"],
+                  cu_seqlens=t["cu_seqlens"], **kw)
+    torch.cuda.synchronize()
+    return [None if x is None else x.float().cpu().numpy().astype(np.float64) for x in out]
+
+
+def reference(d, h0=None):
+    return recurrent(**{k: d[k] for k in FIELDS}, scale=d["scale"], h0=d["h0"] if h0 is None else h0,
+                     cu_seqlens=d["cu_seqlens"])
+
+
+@pytest.mark.parametrize("seg", [1, 2, 3, 8])
+@pytest.mark.parametrize("K,V", [(128, 64), (128, 48), (128, 80), (64, 128)])
+def test_fixed_length_forced_segments(seg, K, V):
+    d = make_inputs(131, B=2, T=64 * 7 + 13, HQK=2, HV=4, K=K, V=V, has_h0=True)
+    o, ht = run(d, seg_chunks=seg)
+    o_ref, ht_ref = reference(d)
+    eo, eh = nerr(o, o_ref), nerr(ht, ht_ref)
+    print(f"  seg {seg} K{K} V{V}: o {eo:.2e} ht {eh:.2e}", flush=True)
+    assert np.all(np.isfinite(o)) and eo <= TOL and eh <= TOL
+
+
+@pytest.mark.parametrize("seg", [1, 2])
+def test_varlen_forced_segments_with_empty_and_short_sequences(seg):
+    d = make_inputs(132, B=1, T=0, HQK=1, HV=2, K=128, V=128, has_h0=True,
+                    lengths=[300, 0, 64, 1, 520, 65])
+    o, ht = run(d, seg_chunks=seg)
+    o_ref, ht_ref = reference(d)
+    eo, eh = nerr(o, o_ref), nerr(ht, ht_ref)
+    print(f"  varlen seg {seg}: o {eo:.2e} ht {eh:.2e}", flush=True)
+    assert eo <= TOL and eh <= TOL
+    assert np.array_equal(ht[1], d["h0"][1].astype(np.float64))     # empty sequence: ht = h0
+
+
+def test_segment_length_changes_only_rounding():
+    d = make_inputs(133, B=1, T=64 * 12, HQK=1, HV=2, K=128, V=64, has_h0=True)
+    outs = [run(d, seg_chunks=s) for s in (1, 4, 12)]
+    for o, ht in outs[1:]:
+        assert nerr(o, outs[0][0]) <= 5e-3 and nerr(ht, outs[0][1]) <= 5e-3
+
+
+def test_chunk_states_and_bf16_state_across_segments():
+    import torch
+    d = make_inputs(134, B=1, T=0, HQK=2, HV=2, K=128, V=64, has_h0=True, lengths=[257, 130, 0, 64])
+    o, ht, hc = run(d, seg_chunks=2, output_chunk_states=True)
+    _, _, inter = chunked(**{k: d[k] for k in FIELDS}, scale=d["scale"], h0=d["h0"],
+                          cu_seqlens=d["cu_seqlens"], return_intermediates=True)
+    hc_ref = np.stack([c["h"] for c in inter])
+    assert hc.shape == hc_ref.shape
+    assert nerr(hc, hc_ref) <= TOL
+    o_ref, ht_ref = reference(d)
+    assert nerr(o, o_ref) <= TOL and nerr(ht, ht_ref) <= TOL
+    # bf16 state I/O with several segments
+    h0_bf = round_to_bf16(d["h0"])
+    t = to_device(d)
+    t["h0"] = torch.from_numpy(h0_bf).to(torch.bfloat16).cuda()
+    o2, ht2 = run(d, t, seg_chunks=1, state_dtype=torch.bfloat16)
+    o2_ref, ht2_ref = reference(d, h0=h0_bf)
+    assert nerr(o2, o2_ref) <= TOL and nerr(ht2, ht2_ref) <= TOL
+    assert np.array_equal(ht2, round_to_bf16(ht2))
+
+
+def test_many_segments_long_sequence_k64():
+    # 40 chunks, one chunk per segment: the prologue chain runs up to 38 products
+    d = make_inputs(135, B=1, T=64 * 40, HQK=1, HV=1, K=64, V=64, has_h0=True, g_mean=4.0)
+    o, ht = run(d, seg_chunks=1)
+    o_ref, ht_ref = reference(d)
+    eo, eh = nerr(o, o_ref), nerr(ht, ht_ref)
+    print(f"  40 segments: o {eo:.2e} ht {eh:.2e}", flush=True)
+    assert eo <= TOL and eh <= TOL
+
+
+def test_automatic_segmented_scan_long_sequence_few_heads():
+    # 2 value heads x 8 tiles of 16 columns, 66 chunks: the library picks the
+    # segmented scan (L = 9, 8 segments)
+    d = make_inputs(136, B=1, T=4200, HQK=2, HV=2, K=128, V=128, has_h0=True)
+    o, ht = run(d)
+    o_ref, ht_ref = reference(d)
+    eo, eh = nerr(o, o_ref), nerr(ht, ht_ref)
+    print(f"  auto segmented: o {eo:.2e} ht {eh:.2e}", flush=True)
+    assert eo <= TOL and eh <= TOL
