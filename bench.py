@@ -1,6 +1,7 @@
 """Benchmark of the KDA chunked forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--config N] [--seg-chunks L]
 
 Workload: the 8192-token prefill, B=1, T=8192, H=32 (q/k and value heads),
 K=V=128, chunk 64, bf16 I/O, h0 = 0, seeded synthetic inputs (synth/).
@@ -45,6 +46,8 @@ KERNEL_SOURCES = {
     "intra": ["gated_delta_rule_chunked_amd/csrc/kda_intra.hip", "gated_delta_rule_chunked_amd/csrc/kda_device.hpp"],
     "inter": ["gated_delta_rule_chunked_amd/csrc/kda_inter.hip", "gated_delta_rule_chunked_amd/csrc/kda_device.hpp"],
     "bwd_dhu": ["gated_delta_rule_chunked_amd/csrc/kda_bwd.hip", "gated_delta_rule_chunked_amd/csrc/kda_device.hpp"],
+    "scan_state": ["gated_delta_rule_chunked_amd/csrc/kda_scan.hip", "gated_delta_rule_chunked_amd/csrc/kda_device.hpp"],
+    "scan_full": ["gated_delta_rule_chunked_amd/csrc/kda_scan.hip", "gated_delta_rule_chunked_amd/csrc/kda_device.hpp"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
@@ -64,16 +67,20 @@ def source_sha(kernel):
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
-    when it is missing or was taken on a different version of the kernel."""
+def traffic_for(workload, call):
+    """HBM bytes per call from the committed rocprofv3 counter summary: the sum over
+    the kernels the call launched for this workload ("intra"; the scan call is the
+    serial scan or the segmented scan's passes), or None when the workload is missing
+    or any of its kernels was measured on a different version of its source."""
+    kernels = {"intra": ["intra"], "inter": ["inter", "scan_state", "scan_full"], "bwd_dhu": ["bwd_dhu"]}[call]
     try:
-        t = json.load(open(TRAFFIC_FILE))[kernel]
+        w = json.load(open(TRAFFIC_FILE))["workloads"][workload]
     except (OSError, KeyError, ValueError):
         return None
-    if t.get("source_sha") != source_sha(kernel):
+    found = [w[k] for k in kernels if k in w]
+    if not found or any(t.get("source_sha") != source_sha(k) for k, t in zip([k for k in kernels if k in w], found)):
         return None
-    return t["bytes_per_launch"]
+    return sum(t["bytes_per_launch"] for t in found)
 
 
 def cpu_baseline(d, budget_s=12.0):
@@ -104,7 +111,7 @@ def bwd_algorithmic_bytes(B, T, HV, K, V, N, C):
             + 2 * N * HV * K * V * 4)               # dht, dh0
 
 
-def bench_bwd(t, d, dev, stream, steps):
+def bench_bwd(t, d, dev, stream, steps, workload):
     """Time kda_bwd_dhu at the workload's shape; returns the bwd_dhu object."""
     import torch
     from gated_delta_rule_chunked_amd import KDA_FLAG_CKPT_BF16, kda_bwd_dhu_raw, make_bwd_args, num_chunks
@@ -145,7 +152,8 @@ def bench_bwd(t, d, dev, stream, steps):
     flops = 6 * K * V * B * T * HV       # DV, QD, WD per token and head
     return {"ms": ms, "tokens_per_s": B * T / (ms * 1e-3), "algorithmic_bytes": nbytes,
             "roofline": {"bound": "hbm", "kernel": "bwd_dhu", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for("bwd_dhu")},
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                         "traffic": traffic_for(workload, "bwd_dhu")},
             "mfma_frac": flops / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
             "checkpoints": "bf16", "states": "fp32", "data": "synthetic stand-ins for qg, kg, w, g2, do, dv, dht"}
 
@@ -159,6 +167,10 @@ def main():
     ap.add_argument("--no-variants", action="store_true", help="skip timing the forward's options")
     ap.add_argument("--cold", type=int, default=20, help="extra cold-cache steps (flush between)")
     ap.add_argument("--no-bwd", action="store_true", help="skip timing the backward state scan")
+    ap.add_argument("--config", type=int, default=CFG_ID, choices=sorted(range(1, 6)),
+                    help="workload (synth/inputs.py CONFIGS); the headline metric is quoted on 3")
+    ap.add_argument("--seg-chunks", type=int, default=0,
+                    help="segment length of the state scan (0: the library's choice)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -173,14 +185,16 @@ def main():
 
     load_library()
     dev = torch.device("cuda:0")
-    d = make_config_inputs(CFG_ID)
+    d = make_config_inputs(args.config)
     t = {k: torch.from_numpy(d[k]).to(torch.bfloat16).to(dev) for k in ("q", "k", "v", "g", "beta")}
+    h0 = None if d["h0"] is None else torch.from_numpy(d["h0"]).to(dev)
+    cu = None if d["cu_seqlens"] is None else torch.from_numpy(d["cu_seqlens"]).to(dev)
     B, T, HV, K, V, N = d["B"], d["T"], d["HV"], d["K"], d["V"], d["N"]
     o = torch.empty((B, T, HV, V), dtype=torch.bfloat16, device=dev)
     ht = torch.empty((N, HV, K, V), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    a = make_args(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], None, None, o, ht,
-                  stream=stream.cuda_stream)
+    a = make_args(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], h0, cu, o, ht,
+                  stream=stream.cuda_stream, seg_chunks=args.seg_chunks)
     ws = alloc_workspace(a, dev)
     a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
 
@@ -236,13 +250,14 @@ def main():
         from gated_delta_rule_chunked_amd import KDA_FLAG_BETA_LOGITS, KDA_FLAG_STATE_BF16, num_chunks
         variants_ms = {}
         ht_bf = torch.empty((N, HV, K, V), dtype=torch.bfloat16, device=dev)
-        hc = torch.empty((num_chunks(T, None, B), HV, K, V), dtype=torch.float32, device=dev)
+        hc = torch.empty((num_chunks(T, cu, B), HV, K, V), dtype=torch.float32, device=dev)
         for name, kw in (("beta_logits", dict(flags=KDA_FLAG_BETA_LOGITS, ht=ht)),
                          ("bf16_state", dict(flags=KDA_FLAG_STATE_BF16, ht=ht_bf)),
                          ("chunk_states_fp32", dict(flags=0, ht=ht, hc=hc))):
             ht_v = kw.pop("ht")
-            av = make_args(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], None, None, o, ht_v,
-                           stream=stream.cuda_stream, **kw)
+            h0v = None if h0 is None else h0.to(ht_v.dtype)
+            av = make_args(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], h0v, cu, o, ht_v,
+                           stream=stream.cuda_stream, seg_chunks=args.seg_chunks, **kw)
             av.workspace, av.workspace_bytes = ws.data_ptr(), ws.numel()
             for _ in range(2):
                 kda_fwd_intra(av)
@@ -257,7 +272,10 @@ def main():
             variants_ms[name] = e0.elapsed_time(e1) / 10
         del hc, ht_bf
 
-    bwd = None if args.no_bwd else bench_bwd(t, d, dev, stream, args.steps)
+    # the backward's stand-in operands are built for fixed-length, whole-chunk sequences
+    bwd = None
+    if not args.no_bwd and d["cu_seqlens"] is None and d["T"] % 64 == 0:
+        bwd = bench_bwd(t, d, dev, stream, args.steps, CONFIGS[args.config].name)
 
     tokens = B * T
     value = tokens / (ms_per_step * 1e-3)
@@ -266,7 +284,8 @@ def main():
     dom = max(kern, key=lambda k: kern[k][0])
     dom_ms, dom_bytes = kern[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    traffic = traffic_for(dom)
+    workload = CONFIGS[args.config].name + (f"_seg{args.seg_chunks}" if args.seg_chunks else "")
+    traffic = traffic_for(workload, dom)
     path_bytes = ab_intra + ab_inter
     flops = FLOPS_PER_TOKEN_HEAD * tokens * HV
     result = {
@@ -282,8 +301,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": CONFIGS[CFG_ID].name, "B": B, "T": T, "HQK": d["HQK"], "HV": HV, "K": K,
-                   "V": V, "chunk": 64, "h0": "zero"},
+        "config": {"workload": CONFIGS[args.config].name, "B": B, "T": T, "N": d["N"], "HQK": d["HQK"], "HV": HV,
+                   "K": K, "V": V, "chunk": 64, "h0": "zero" if d["h0"] is None else "0.1 N(0,1)",
+                   "varlen": d["cu_seqlens"] is not None, "seg_chunks": args.seg_chunks},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
         "kernels_ms": {"intra": kern["intra"][0], "inter": kern["inter"][0]},
