@@ -1,12 +1,19 @@
 """Benchmark of the KDA chunked forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--config N] [--seg-chunks L]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-s S]
+                    [--no-cpu-baseline] [--config N] [--seg-chunks L]
 
 Workload: the 8192-token prefill, B=1, T=8192, H=32 (q/k and value heads),
 K=V=128, chunk 64, bf16 I/O, h0 = 0, seeded synthetic inputs (synth/).
 A step is one call of the whole hot path (intra-chunk kernel, then the
 inter-chunk state scan) on inputs already resident in HBM.  Prints one JSON line.
+
+Timing: W warmup steps, continued for at least --settle-s seconds so that the GPU
+clocks have ramped up; then K steps between two device synchronizations on the
+wall clock (ms_per_step, value).  Inside the same region every step records two
+HIP events (before each of its two calls) created with hipEventDisableSystemFence,
+which give the per-kernel durations for the roofline without the system-scope cache
+flush a default event record costs.
 
 Algorithmic bytes per token and value head (K = V = 128): q, k, g, v, o at 256 B
 each plus beta 2 B = 1,282 B (q, k per q/k head), plus the final state ht once per
@@ -50,6 +57,49 @@ KERNEL_SOURCES = {
     "scan_full": ["gated_delta_rule_chunked_amd/csrc/kda_scan.hip", "gated_delta_rule_chunked_amd/csrc/kda_device.hpp"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hip_runtime_api.h
+
+
+class HipEvents:
+    """Timing events of the HIP runtime that torch (and libkda) already loaded,
+    created with hipEventDisableSystemFence: recording one then costs no system-scope
+    cache write-back and invalidation, which torch's default events pay (several us
+    per record on MI355X, inflating the steps they bracket)."""
+
+    def __init__(self, n):
+        import ctypes
+        self._c = ctypes
+        hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
+        vp = ctypes.c_void_p
+        hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+        hip.hipEventRecord.argtypes = [vp, vp]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        hip.hipEventDestroy.argtypes = [vp]
+        self._hip = hip
+        self.ev = []
+        for _ in range(n):
+            e = vp()
+            st = hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE)
+            if st != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed with status {st}")
+            self.ev.append(e)
+
+    def record(self, i, stream):
+        st = self._hip.hipEventRecord(self.ev[i], self._c.c_void_p(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord failed with status {st}")
+
+    def ms(self, i, j):
+        """Milliseconds from event i to event j (both complete)."""
+        f = self._c.c_float()
+        st = self._hip.hipEventElapsedTime(self._c.byref(f), self.ev[i], self.ev[j])
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed with status {st}")
+        return f.value
+
+    def __del__(self):
+        for e in getattr(self, "ev", []):
+            self._hip.hipEventDestroy(e)
 
 
 def algorithmic_bytes(d):
@@ -140,13 +190,13 @@ def bench_bwd(t, d, dev, stream, steps, workload):
     for _ in range(3):
         kda_bwd_dhu_raw(a)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for e0, e1 in evs:
-        e0.record(stream)
+    ev = HipEvents(steps + 1)   # call i runs between events i and i + 1
+    for i in range(steps):
+        ev.record(i, stream)
         kda_bwd_dhu_raw(a)
-        e1.record(stream)
+    ev.record(steps, stream)
     torch.cuda.synchronize()
-    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    ms = float(np.mean([ev.ms(i, i + 1) for i in range(steps)]))
     nbytes = bwd_algorithmic_bytes(B, T, HV, K, V, N, C)
     achieved = nbytes / (ms * 1e-3) / 1e9
     flops = 6 * K * V * B * T * HV       # DV, QD, WD per token and head
@@ -163,6 +213,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="keep warming up until this many seconds have passed (GPU clocks ramp up under load)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true", help="skip timing the forward's options")
     ap.add_argument("--cold", type=int, default=20, help="extra cold-cache steps (flush between)")
@@ -203,29 +255,36 @@ def main():
     calib_dst = torch.empty_like(calib_src)
     calib_dst.copy_(calib_src)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    # Step i of the timed region: event 2i, intra call, event 2i+1, inter call; event
+    # 2K closes the last one, so two events per step time both calls.
+    ev = HipEvents(2 * args.steps + 1)
+
+    def step(i=None):
+        if i is not None:
+            ev.record(2 * i, stream)
         kda_fwd_intra(a)
-        if ev is not None:
-            ev[1].record(stream)
+        if i is not None:
+            ev.record(2 * i + 1, stream)
         kda_fwd_inter(a)
-        if ev is not None:
-            ev[2].record(stream)
 
-    for _ in range(args.warmup):
+    # W warmup steps, continued until the clocks have settled (--settle-s of steps)
+    t0 = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or time.perf_counter() - t0 < args.settle_s:
         step()
+        n_warm += 1
+        if n_warm % 64 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        step(i)
+    ev.record(2 * args.steps, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    intra_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    inter_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    intra_ms = np.array([ev.ms(2 * i, 2 * i + 1) for i in range(args.steps)])
+    inter_ms = np.array([ev.ms(2 * i + 1, 2 * i + 2) for i in range(args.steps)])
     ms_per_step = wall * 1e3 / args.steps
 
     # cold-cache steps: a 1 GiB buffer written between steps evicts L2 and MALL
@@ -233,14 +292,14 @@ def main():
     if args.cold:
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         cold = []
+        cev = HipEvents(2)
         for _ in range(args.cold):
             flush.fill_(1)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+            cev.record(0, stream)
             step()
-            e1.record(stream)
+            cev.record(1, stream)
             torch.cuda.synchronize()
-            cold.append(e0.elapsed_time(e1))
+            cold.append(cev.ms(0, 1))
         cold_ms = float(np.median(cold))
         del flush
 
@@ -262,14 +321,14 @@ def main():
             for _ in range(2):
                 kda_fwd_intra(av)
                 kda_fwd_inter(av)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+            vev = HipEvents(2)
+            vev.record(0, stream)
             for _ in range(10):
                 kda_fwd_intra(av)
                 kda_fwd_inter(av)
-            e1.record(stream)
+            vev.record(1, stream)
             torch.cuda.synchronize()
-            variants_ms[name] = e0.elapsed_time(e1) / 10
+            variants_ms[name] = vev.ms(0, 1) / 10
         del hc, ht_bf
 
     # the backward's stand-in operands are built for fixed-length, whole-chunk sequences
@@ -295,6 +354,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": n_warm,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
