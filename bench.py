@@ -10,10 +10,11 @@ inter-chunk state scan) on inputs already resident in HBM.  Prints one JSON line
 
 Timing: W warmup steps, continued for at least --settle-s seconds so that the GPU
 clocks have ramped up; then K steps between two device synchronizations on the
-wall clock (ms_per_step, value).  Inside the same region every step records two
-HIP events (before each of its two calls) created with hipEventDisableSystemFence,
-which give the per-kernel durations for the roofline without the system-scope cache
-flush a default event record costs.
+wall clock (ms_per_step, value).  Inside the same region every fourth step
+(--event-every) records HIP events around each of its two calls, created with
+hipEventDisableSystemFence; they give the per-kernel durations for the roofline
+without the system-scope cache flush a default event record costs.  Each record
+still costs a few microseconds of device time, hence the sampling.
 
 Algorithmic bytes per token and value head (K = V = 128): q, k, g, v, o at 256 B
 each plus beta 2 B = 1,282 B (q, k per q/k head), plus the final state ht once per
@@ -213,6 +214,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--event-every", type=int, default=4,
+                    help="time the two calls of every n-th timed step with events (each record costs ~2.5 us)")
     ap.add_argument("--settle-s", type=float, default=1.0,
                     help="keep warming up until this many seconds have passed (GPU clocks ramp up under load)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -255,17 +258,22 @@ def main():
     calib_dst = torch.empty_like(calib_src)
     calib_dst.copy_(calib_src)
 
-    # Step i of the timed region: event 2i, intra call, event 2i+1, inter call; event
-    # 2K closes the last one, so two events per step time both calls.
-    ev = HipEvents(2 * args.steps + 1)
+    # Every --event-every-th step of the timed region is bracketed by events: 3j before
+    # its intra call, 3j+1 before its inter call, 3j+2 after it.
+    sampled = list(range(0, args.steps, max(1, args.event_every)))
+    ev = HipEvents(3 * len(sampled))
+    slot = {i: j for j, i in enumerate(sampled)}
 
     def step(i=None):
-        if i is not None:
-            ev.record(2 * i, stream)
+        j = slot.get(i)
+        if j is not None:
+            ev.record(3 * j, stream)
         kda_fwd_intra(a)
-        if i is not None:
-            ev.record(2 * i + 1, stream)
+        if j is not None:
+            ev.record(3 * j + 1, stream)
         kda_fwd_inter(a)
+        if j is not None:
+            ev.record(3 * j + 2, stream)
 
     # W warmup steps, continued until the clocks have settled (--settle-s of steps)
     t0 = time.perf_counter()
@@ -280,12 +288,20 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
-    ev.record(2 * args.steps, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    intra_ms = np.array([ev.ms(2 * i, 2 * i + 1) for i in range(args.steps)])
-    inter_ms = np.array([ev.ms(2 * i + 1, 2 * i + 2) for i in range(args.steps)])
+    intra_ms = np.array([ev.ms(3 * j, 3 * j + 1) for j in range(len(sampled))])
+    inter_ms = np.array([ev.ms(3 * j + 1, 3 * j + 2) for j in range(len(sampled))])
     ms_per_step = wall * 1e3 / args.steps
+
+    # the box's device-copy bandwidth (bytes read + written per second), for context
+    cev = HipEvents(2)
+    cev.record(0, stream)
+    for _ in range(5):
+        calib_dst.copy_(calib_src)
+    cev.record(1, stream)
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * calib_src.numel() / (cev.ms(0, 1) * 1e-3) / 1e9
 
     # cold-cache steps: a 1 GiB buffer written between steps evicts L2 and MALL
     cold_ms = None
@@ -355,6 +371,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "warmup_steps_run": n_warm,
+        "event_timed_steps": len(sampled),
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -367,6 +384,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
         "kernels_ms": {"intra": kern["intra"][0], "inter": kern["inter"][0]},
+        "step_ms_p10_p50_p90": [float(x) for x in np.percentile(intra_ms + inter_ms, [10, 50, 90])],
+        "device_copy_GBs": copy_gbs,
         "path_roofline": {"algorithmic_bytes": path_bytes,
                           "hbm_frac": path_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
                           "mfma_frac": flops / (ms_per_step * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12)},
