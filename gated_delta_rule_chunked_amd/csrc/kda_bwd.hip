@@ -330,8 +330,9 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dhu_kernel(BwdParams p, in
   } else {
     // ============================ loader waves ============================
     // Loader lw moves operand lw (kg, qg, w) of a chunk: piece i of this lane is
-    // row 16 (i & 3) + (ln >> 2), columns 8 (4 (i >> 2) + (ln & 3)) .. +7, so one
-    // load instruction covers 16 rows x 64 contiguous bytes.
+    // row 8 (i & 7) + (ln >> 3), columns 64 (i >> 3) + 8 (ln & 7) .. +7, so one load
+    // instruction covers 8 rows x 128 contiguous bytes, whole cache lines (16 rows x
+    // 64 bytes, half lines, measured 2.4 % slower).
     constexpr int NLD = BT * K / 8 / 64;     // 16-byte pieces per lane and chunk
     const int lw = wave - 5;
     const uint16_t* X = lw == 0 ? p.kg : (lw == 1 ? p.qg : p.w);
@@ -340,27 +341,27 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dhu_kernel(BwdParams p, in
       for (int ph = 0; ph <= nphase; ++ph) barrier_lds();
       return;
     }
-    const int lrow = ln >> 2, lcol = 8 * (ln & 3);
+    const int lrow = ln >> 3, lcol = 8 * (ln & 7);
     const uint16_t* Xb = X + (row0 * p.HV + hv) * K + lcol;
     const int64_t rstride = (int64_t)p.HV * K;
     auto fetch = [&](int ph, u32x4* dst) {
       const int c = chunk_of(ph);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {          // the four rows of this lane
-        const uint16_t* a = Xb + (int64_t)min(c * BT + 16 * q + lrow, sq.len - 1) * rstride;
+      for (int q = 0; q < 8; ++q) {          // the eight rows of this lane
+        const uint16_t* a = Xb + (int64_t)min(c * BT + 8 * q + lrow, sq.len - 1) * rstride;
 #pragma unroll
-        for (int i = q; i < NLD; i += 4) dst[i] = *reinterpret_cast<const u32x4*>(a + 32 * (i >> 2));
+        for (int i = q; i < NLD; i += 8) dst[i] = *reinterpret_cast<const u32x4*>(a + 64 * (i >> 3));
       }
     };
     auto put = [&](int ph, const u32x4* src) {
       const int c = chunk_of(ph);
       uint8_t* dst = smem + (ph & 1) * SM::STAGE + off + (lrow * SM::RS + lcol) * 2;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bool ok = c * BT + 16 * q + lrow < sq.len;
+      for (int q = 0; q < 8; ++q) {
+        const bool ok = c * BT + 8 * q + lrow < sq.len;
 #pragma unroll
-        for (int i = q; i < NLD; i += 4)
-          *reinterpret_cast<u32x4*>(dst + (16 * q * SM::RS + 32 * (i >> 2)) * 2) = ok ? src[i] : u32x4{0, 0, 0, 0};
+        for (int i = q; i < NLD; i += 8)
+          *reinterpret_cast<u32x4*>(dst + (8 * q * SM::RS + 64 * (i >> 3)) * 2) = ok ? src[i] : u32x4{0, 0, 0, 0};
       }
     };
     u32x4 ra[NLD], rb[NLD], rc[NLD];
