@@ -29,7 +29,8 @@
 //   waves 0-3 (column waves): wave c holds h for columns 16c..16c+15 of the group
 //     in the C layout of 16x16 MFMA tiles and runs the whole chunk in registers:
 //     u, v', the update of h and (full pass) o^T = h^T qg^T + v'^T Aqk^T, whose C
-//     layout gives each lane four adjacent columns of one token (8-byte stores).
+//     layout gives each lane four adjacent columns of one token; the four waves
+//     stage o in LDS and store it as whole 128-byte rows during the next chunk.
 //     Operands come from the staged record; v^T fragments by transpose reads of the
 //     row-major v tile.
 //   waves 4-7 (loader waves): keep three chunks of records in flight in a register
@@ -55,7 +56,12 @@ struct ScanSmem {
   static constexpr int SLOT = NSTEP * 1024;
   static constexpr int VT = 2 * SLOT;                // v tiles: [2 slots][4 column waves][64][16] bf16
   static constexpr int VT_BYTES = BT * BV * 2;
-  static constexpr int BYTES = VT + (MODE == SCAN_M ? 0 : 2 * 4 * VT_BYTES);
+  // full pass: o of a chunk staged as [64 rows][64 columns] bf16 (rows padded to 144
+  // bytes), two buffers, so that it leaves in whole 128-byte rows
+  static constexpr int OST = VT + (MODE == SCAN_M ? 0 : 2 * 4 * VT_BYTES);
+  static constexpr int OSTR = 144;
+  static constexpr int OST_BYTES = BT * OSTR;
+  static constexpr int BYTES = OST + (MODE == SCAN_FULL ? 2 * OST_BYTES : 0);
   static_assert(BYTES <= 160 * 1024, "fits the LDS of one CU");
 };
 
@@ -243,10 +249,28 @@ __device__ __forceinline__ void scan_body(const Params& p, uint8_t* smem, const 
   // per-lane parts of the LDS addresses of the v tile's transpose reads
   const int tr16 = ((4 * (ln >> 4) + ((ln >> 2) & 3)) * BV + 4 * (ln & 3)) * 2;
   // o: this lane's columns in the sequence's first row, and the row stride
-  const int orow = p.HV * p.V;
-  uint16_t* const obase = p.o + (row0 * p.HV + hv) * p.V + grp * 64 + BV * cw + 4 * g;
+  // o of the chunk of phase q, staged in buffer q & 1, leaves in whole rows at the
+  // start of the next phase: lane (row 8 h + (ln >> 3), 16-byte column block ln & 7),
+  // row blocks h shared out over the active column waves; columns past V are never
+  // written.  Each column wave storing its own 32-byte row segments directly was
+  // measured 8 % slower over the whole scan.
+  auto store_o = [&](int q) {
+    const int c = sl.c0 + q;
+    const uint8_t* ob = smem + SM::OST + (q & 1) * SM::OST_BYTES;
+    const int lc = ln & 7;
+    if (lc < 2 * ntiles) {
+      for (int h8 = cw; h8 < 8; h8 += ntiles) {
+        const int row = 8 * h8 + (ln >> 3);
+        if (c * BT + row < sl.len) {
+          const uint4 v = *reinterpret_cast<const uint4*>(ob + row * SM::OSTR + 16 * lc);
+          *reinterpret_cast<uint4*>(p.o + ((row0 + c * BT + row) * p.HV + hv) * p.V + grp * 64 + 8 * lc) = v;
+        }
+      }
+    }
+  };
   barrier_lds();  // S0
   for (int ph = 0; ph < nphase; ++ph) {
+    if (MODE == SCAN_FULL && ph >= 1 && ph <= ncs) store_o(ph - 1);
     if (ph < ncs) {
       const int c = sl.c0 + ph;
       if (MODE == SCAN_FULL && p.hc) {   // the state before this chunk
@@ -360,14 +384,14 @@ __device__ __forceinline__ void scan_body(const Params& p, uint8_t* smem, const 
           if (tri_steps(w) > 1) oacc2 = mfma16x32(vp1, as_frag(aq[1]), oacc2);
           ov[w] = pack4(oacc + oacc2);
         }
-        uint16_t* oc = obase + (int64_t)(c * BT) * orow;      // this chunk's first row
+        uint8_t* ob = smem + SM::OST + (ph & 1) * SM::OST_BYTES + (16 * cw + 4 * g) * 2;
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
-          if (c * BT + 16 * w + r < sl.len) *reinterpret_cast<uint2*>(oc + (16 * w + r) * orow) = ov[w];
+        for (int w = 0; w < 4; ++w) *reinterpret_cast<uint2*>(ob + (16 * w + r) * SM::OSTR) = ov[w];
       }
     }
     barrier_lds();
   }
+  if (MODE == SCAN_FULL && ncs == nphase && ncs > 0) store_o(ncs - 1);   // no spare phase left for it
   // the segment's end state
   if (MODE == SCAN_B) {
     float* bb = p.bbuf + ((sigma * p.HV + hv) * K) * (int64_t)p.V + col;
