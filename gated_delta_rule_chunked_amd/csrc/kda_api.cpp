@@ -77,9 +77,18 @@ int check_shapes(const kda_fwd_args* a, kda::WsLayout* L) {
   } else {
     const int64_t cus = kda::device_cus();
     const int64_t units64 = (int64_t)a->N * a->HV * ((a->V + 63) / 64);
+    // chunks per sequence (the mean for varlen, where the lengths stay on the device)
+    const int64_t per_seq = a->cu_seqlens ? nt / std::max<int64_t>(a->N, 1) : nt;
     if (units64 >= cus) {            // 64-column workgroups alone fill the device: one segment each
       seg_path = true;
       seg_L = std::max<int64_t>(nt, 1);
+    } else if (per_seq >= 128) {
+      // long sequences: as many segments per sequence (2 to 8) as one round of the
+      // full pass's 64-column workgroups allows; measured faster than the 16-column
+      // serial scan from 16 to 64 heads at 8,192 tokens and at 16,384 and 32,768
+      seg_path = true;
+      const int64_t S = std::min<int64_t>(8, std::max<int64_t>(2, cus / units64));
+      seg_L = (per_seq + S - 1) / S;
     } else {
       seg_path = units16 * 2 < cus && nt >= 64;
       seg_L = std::max<int64_t>(8, (nt + 7) / 8);

@@ -72,14 +72,22 @@ def ws(a):
 
 def test_workspace_bytes(lib):
     # [header | records | (segmented scan: 1 KiB pad | B | M)]: records are one per
-    # (chunk, value head).  The serial scan is chosen when N x HV x V/16 >= half of
-    # the compute units (256 when no device is seen) or there are fewer than 64
-    # chunks; the segmented scan adds one B (fp32 K x V) and one M (bf16 K x K) per
-    # (segment, value head) when a sequence has more than one segment.
+    # (chunk, value head).  With 256 compute units (no device seen): one segment per
+    # sequence when N x HV x V/64 >= 256; else, for sequences of 128 chunks or more,
+    # S = clamp(256 / (N x HV x V/64), 2, 8) segments; else the serial scan when
+    # N x HV x V/16 >= 128 or there are fewer than 64 chunks.  The segmented scan adds
+    # one B (fp32 K x V) and one M (bf16 K x K) per (segment, value head) when a
+    # sequence has more than one segment.
     KV4, KK2 = 128 * 128 * 4, 128 * 128 * 2
-    # T=8192, H=32, K=V=128: 256 serial workgroups -> serial scan
+    # T=8192, H=32, K=V=128: 128 chunks, 64 wide workgroups -> 4 segments of 32 chunks
     st, n = ws(args(B=1, T=8192, HQK=32, HV=32))
-    assert st == 0 and n == 256 + 128 * 32 * 61952
+    assert st == 0 and n == 256 + 128 * 32 * 61952 + 1024 + 4 * 32 * (KV4 + KK2)
+    # T=4096, H=32: 64 chunks, 256 serial workgroups -> serial scan
+    st, n = ws(args(B=1, T=4096, HQK=32, HV=32))
+    assert st == 0 and n == 256 + 64 * 32 * 61952
+    # T=8192, H=48: 96 wide workgroups -> 2 segments of 64 chunks
+    st, n = ws(args(B=1, T=8192, HQK=48, HV=48))
+    assert st == 0 and n == 256 + 128 * 48 * 61952 + 1024 + 2 * 48 * (KV4 + KK2)
     st, n = ws(args(B=2, T=200, HQK=1, HV=1, K=64, V=64, N=2))
     assert st == 0 and n == 256 + 2 * 4 * 37120
     # varlen: chunk table (N + 2 int32) and per-chunk info (8 bytes per chunk of the
