@@ -114,10 +114,12 @@ __device__ __forceinline__ bool locate_segment(const Params& p, int64_t sigma, S
 
 // The chunks of one segment for one value head and 64-column group (`grp`: value
 // columns 64 grp.., or key columns 64 grp.. of M in SCAN_M), with `ntiles` active
-// column waves.
+// column waves.  Waves from `lwave0` on are the loader waves; column wave cw is wave
+// `cwave0` + cw (the state pass runs the b and M column waves of a group in one
+// workgroup, each set through its own instantiation, over one set of loaders).
 template <int K, int MODE>
 __device__ __forceinline__ void scan_body(const Params& p, uint8_t* smem, const SegLoc& sl, int hv, int grp,
-                                          int ntiles, int64_t sigma) {
+                                          int ntiles, int64_t sigma, int lwave0 = 4, int cwave0 = 0) {
   using SM = ScanSmem<K, MODE>;
   using R = Rec<K>;
   constexpr int S = K / 32, ND = K / 16;
@@ -129,10 +131,10 @@ __device__ __forceinline__ void scan_body(const Params& p, uint8_t* smem, const 
   const int64_t row0 = (int64_t)sl.b * p.T + sl.bos;        // first token row of the sequence
   auto chunk_of = [&](int ph) { return sl.c0 + min(ph, ncs - 1); };   // tail phases re-read the last chunk
 
-  if (wave >= 4) {
+  if (wave >= lwave0) {
     // ============================ loader waves ============================
     constexpr int NLD = SM::NLD;
-    const int lw = wave - 4;
+    const int lw = wave - lwave0;
     if (ncs == 0) {
       barrier_lds();  // S0
       return;
@@ -195,7 +197,7 @@ __device__ __forceinline__ void scan_body(const Params& p, uint8_t* smem, const 
   }
 
   // ============================ column waves ============================
-  const int cw = wave;
+  const int cw = wave - cwave0;
   if (cw >= ntiles) {                         // columns past V: keep the barrier count only
     for (int ph = 0; ph <= nphase; ++ph) barrier_lds();
     return;
@@ -336,10 +338,14 @@ __device__ __forceinline__ void scan_body(const Params& p, uint8_t* smem, const 
         h[md][3] *= al[md].w;
       }
       __builtin_amdgcn_sched_barrier(0);
-      // batch 2: kg^T
+      // batch 2: kg^T, ahead of the v' products in the full pass; in the state pass
+      // (twelve waves, 168 registers) only after them, when the -w fragments are dead
       uint4 kg[2 * ND];
+      auto load_kg = [&]() {
 #pragma unroll
-      for (int i = 0; i < 2 * ND; ++i) kg[i] = lds16(st + R::KGT + (i * 64 + ln) * 16);
+        for (int i = 0; i < 2 * ND; ++i) kg[i] = lds16(st + R::KGT + (i * 64 + ln) * 16);
+      };
+      if (MODE == SCAN_FULL) load_kg();
       __builtin_amdgcn_sched_barrier(0);
       // v' = u + (-w) h
 #pragma unroll
@@ -351,6 +357,10 @@ __device__ __forceinline__ void scan_body(const Params& p, uint8_t* smem, const 
       uint2 vp[4];
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) vp[mb] = pack4(acc[mb]);
+      if (MODE != SCAN_FULL) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_kg();
+      }
       // h <- diag(alpha) h + kg^T v'   (v' tiles (2s2, 2s2+1) = P-order token step s2)
       const bf16x8 vp0 = cat(vp[0], vp[1]), vp1 = cat(vp[2], vp[3]);
 #pragma unroll
@@ -392,19 +402,24 @@ __device__ __forceinline__ void scan_body(const Params& p, uint8_t* smem, const 
     barrier_lds();
   }
   if (MODE == SCAN_FULL && ncs == nphase && ncs > 0) store_o(ncs - 1);   // no spare phase left for it
-  // the segment's end state
+  // the segment's end state (row strides made opaque, so that the 32 row offsets are
+  // not computed ahead of the chunk loop and kept live through it)
   if (MODE == SCAN_B) {
-    float* bb = p.bbuf + ((sigma * p.HV + hv) * K) * (int64_t)p.V + col;
+    int sv = p.V;
+    asm volatile("" : "+s"(sv));
+    float* bb = p.bbuf + ((sigma * p.HV + hv) * K + 4 * g) * (int64_t)sv + col;
 #pragma unroll
     for (int md = 0; md < ND; ++md)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) bb[(int64_t)(16 * md + 4 * g + rr) * p.V] = h[md][rr];
+      for (int rr = 0; rr < 4; ++rr) bb[(int64_t)(16 * md + rr) * sv] = h[md][rr];
   } else if (MODE == SCAN_M) {
-    uint16_t* mm = p.mbuf + (sigma * p.HV + hv) * (int64_t)K * K + col;
+    int sk = K;
+    asm volatile("" : "+s"(sk));
+    uint16_t* mm = p.mbuf + (sigma * p.HV + hv) * (int64_t)K * K + 4 * g * sk + col;
 #pragma unroll
     for (int md = 0; md < ND; ++md)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) mm[(16 * md + 4 * g + rr) * K] = f2bf(h[md][rr]);
+      for (int rr = 0; rr < 4; ++rr) mm[(16 * md + rr) * sk] = f2bf(h[md][rr]);
   } else if (p.ht && sl.s == sl.nseg - 1) {
 #pragma unroll
     for (int md = 0; md < ND; ++md)
@@ -416,27 +431,35 @@ __device__ __forceinline__ void scan_body(const Params& p, uint8_t* smem, const 
   }
 }
 
-// State pass: item = ((sigma * HV + hv) * (NCG + K/64) + j); j < NCG is the b task of
-// value-column group j, j >= NCG the M task of key-column group j - NCG.
+// State pass: item = (sigma * HV + hv) * NJ + j, NJ = max(V/64, K/64) rounded up.  One
+// workgroup of twelve waves computes, over one staged copy of the segment's records,
+// b for value columns 64 j.. (waves 0-3, every segment but a sequence's last) and M
+// for key columns 64 j.. (waves 4-7, inner segments only); waves 8-11 load.  With b and
+// M in separate workgroups the benchmarked shape needed 320 of them, a second round on
+// 256 compute units; paired they are 192.
+constexpr int SCAN_STATE_THREADS = 768;
 template <int K>
-__global__ __launch_bounds__(SCAN_THREADS, 1) void scan_state_kernel(Params p, int n_items) {
+__global__ __launch_bounds__(SCAN_STATE_THREADS, 1) void scan_state_kernel(Params p, int n_items) {
+  static_assert(ScanSmem<K, SCAN_B>::SLOT == ScanSmem<K, SCAN_M>::SLOT, "b and M waves read one staging layout");
   __shared__ __attribute__((aligned(16))) uint8_t smem[ScanSmem<K, SCAN_B>::BYTES];
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   if (item >= n_items) return;
   if (p.cu != nullptr && p.table[p.N + 1] != 0) return;   // rejected cu_seqlens: the full pass reports it
-  const int NCG = (p.V + 63) / 64, NJ = NCG + K / 64;
+  const int NCG = (p.V + 63) / 64, NJ = max(NCG, K / 64);
   const int j = item % NJ;
   const int hv = (item / NJ) % p.HV;
   const int64_t sigma = item / (NJ * p.HV);
   SegLoc sl;
   if (!locate_segment(p, sigma, sl)) return;
-  if (j < NCG) {
-    if (sl.s >= sl.nseg - 1) return;                  // the last segment's end state is not needed
-    scan_body<K, SCAN_B>(p, smem, sl, hv, j, min(4, (p.V - 64 * j) / BV), sigma);
-  } else {
-    if (sl.s == 0 || sl.s >= sl.nseg - 1) return;     // M is needed between inner segments only
-    scan_body<K, SCAN_M>(p, smem, sl, hv, j - NCG, 4, sigma);
-  }
+  const bool inner = sl.s < sl.nseg - 1;                  // the last segment's end state is not needed
+  const int nb = (inner && j < NCG) ? min(4, (p.V - 64 * j) / BV) : 0;
+  const int nm = (inner && sl.s > 0 && j < K / 64) ? 4 : 0;   // M between inner segments only
+  if (nb == 0 && nm == 0) return;                         // uniform over the workgroup
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave >= 4 && wave < 8)
+    scan_body<K, SCAN_M>(p, smem, sl, hv, j, nm, sigma, 8, 4);
+  else   // b column waves and the loaders (which also stage v for the b waves)
+    scan_body<K, SCAN_B>(p, smem, sl, hv, j, nb, sigma, 8, 0);
 }
 
 // Full pass: item = (sigma * HV + hv) * NCG + cg.
@@ -471,8 +494,8 @@ template <int K>
 static hipError_t launch_scan_k(const Params& p, hipStream_t s) {
   const int64_t NCG = (p.V + 63) / 64;
   if (p.bbuf != nullptr) {
-    const int64_t items = p.max_segs * p.HV * (NCG + K / 64);
-    hipLaunchKernelGGL((scan_state_kernel<K>), dim3((int)((items + 7) / 8 * 8)), dim3(SCAN_THREADS), 0, s, p,
+    const int64_t items = p.max_segs * p.HV * std::max<int64_t>(NCG, K / 64);
+    hipLaunchKernelGGL((scan_state_kernel<K>), dim3((int)((items + 7) / 8 * 8)), dim3(SCAN_STATE_THREADS), 0, s, p,
                        (int)items);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
