@@ -338,17 +338,17 @@ def main():
             av = make_args(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], h0v, cu, o, ht_v,
                            stream=stream.cuda_stream, seg_chunks=args.seg_chunks, **kw)
             av.workspace, av.workspace_bytes = ws.data_ptr(), ws.numel()
-            for _ in range(2):
+            for _ in range(20):
                 kda_fwd_intra(av)
                 kda_fwd_inter(av)
             vev = HipEvents(2)
             vev.record(0, stream)
-            for _ in range(10):
+            for _ in range(20):
                 kda_fwd_intra(av)
                 kda_fwd_inter(av)
             vev.record(1, stream)
             torch.cuda.synchronize()
-            variants_ms[name] = vev.ms(0, 1) / 10
+            variants_ms[name] = vev.ms(0, 1) / 20
         del hc, ht_bf
 
     # the backward's stand-in operands are built for fixed-length, whole-chunk sequences

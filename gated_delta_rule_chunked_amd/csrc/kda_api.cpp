@@ -82,10 +82,11 @@ int check_shapes(const kda_fwd_args* a, kda::WsLayout* L) {
     if (units64 >= cus) {            // 64-column workgroups alone fill the device: one segment each
       seg_path = true;
       seg_L = std::max<int64_t>(nt, 1);
-    } else if (per_seq >= 128) {
+    } else if (per_seq >= 96) {
       // long sequences: as many segments per sequence (2 to 8) as one round of the
-      // full pass's 64-column workgroups allows; measured faster than the 16-column
-      // serial scan from 16 to 64 heads at 8,192 tokens and at 16,384 and 32,768
+      // full pass's 64-column workgroups allows; measured at or faster than the
+      // 16-column serial scan from 16 to 64 heads at 6,144 to 32,768 tokens (at 4,096
+      // tokens the two are even)
       seg_path = true;
       const int64_t S = std::min<int64_t>(8, std::max<int64_t>(2, cus / units64));
       seg_L = (per_seq + S - 1) / S;

@@ -73,7 +73,7 @@ def ws(a):
 def test_workspace_bytes(lib):
     # [header | records | (segmented scan: 1 KiB pad | B | M)]: records are one per
     # (chunk, value head).  With 256 compute units (no device seen): one segment per
-    # sequence when N x HV x V/64 >= 256; else, for sequences of 128 chunks or more,
+    # sequence when N x HV x V/64 >= 256; else, for sequences of 96 chunks or more,
     # S = clamp(256 / (N x HV x V/64), 2, 8) segments; else the serial scan when
     # N x HV x V/16 >= 128 or there are fewer than 64 chunks.  The segmented scan adds
     # one B (fp32 K x V) and one M (bf16 K x K) per (segment, value head) when a
@@ -85,6 +85,9 @@ def test_workspace_bytes(lib):
     # T=4096, H=32: 64 chunks, 256 serial workgroups -> serial scan
     st, n = ws(args(B=1, T=4096, HQK=32, HV=32))
     assert st == 0 and n == 256 + 64 * 32 * 61952
+    # T=6144, H=32: 96 chunks -> 4 segments of 24 chunks
+    st, n = ws(args(B=1, T=6144, HQK=32, HV=32))
+    assert st == 0 and n == 256 + 96 * 32 * 61952 + 1024 + 4 * 32 * (KV4 + KK2)
     # T=8192, H=48: 96 wide workgroups -> 2 segments of 64 chunks
     st, n = ws(args(B=1, T=8192, HQK=48, HV=48))
     assert st == 0 and n == 256 + 128 * 48 * 61952 + 1024 + 2 * 48 * (KV4 + KK2)
