@@ -237,8 +237,8 @@ def main():
         sys.exit(2)
 
     import torch
-    from gated_delta_rule_chunked_amd import (alloc_workspace, kda_fwd_inter, kda_fwd_intra, load_library,
-                                              make_args)
+    from gated_delta_rule_chunked_amd import (alloc_workspace, kda_fwd_inter, kda_fwd_intra, kda_fwd_scan_plan,
+                                              load_library, make_args)
     from synth import make_config_inputs
     from synth.inputs import CONFIGS
 
@@ -256,6 +256,7 @@ def main():
                   stream=stream.cuda_stream, seg_chunks=args.seg_chunks)
     ws = alloc_workspace(a, dev)
     a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    plan = kda_fwd_scan_plan(a)   # 0: 16-column serial scan; else 64-column segments of `plan` chunks
 
     # plain copy of known size: the byte-counter calibration kernel for rocprofv3 --pmc
     calib_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -384,7 +385,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": CONFIGS[args.config].name, "B": B, "T": T, "N": d["N"], "HQK": d["HQK"], "HV": HV,
                    "K": K, "V": V, "chunk": 64, "h0": "zero" if d["h0"] is None else "0.1 N(0,1)",
-                   "varlen": d["cu_seqlens"] is not None, "seg_chunks": args.seg_chunks},
+                   "varlen": d["cu_seqlens"] is not None, "seg_chunks": args.seg_chunks,
+                   "scan": "16-column serial" if plan == 0 else f"64-column, segments of {plan} chunks"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
         "kernels_ms": {"intra": kern["intra"][0], "inter": kern["inter"][0]},

@@ -239,6 +239,15 @@ int kda_fwd_workspace_bytes(const kda_fwd_args* a, size_t* bytes) {
   return KDA_OK;
 }
 
+int kda_fwd_scan_plan(const kda_fwd_args* a, int32_t* seg_chunks) {
+  if (!seg_chunks) return KDA_ERR_INVALID_ARG;
+  kda::WsLayout L;
+  int st = check_shapes(a, &L);
+  if (st != KDA_OK) return st;
+  *seg_chunks = L.seg_path ? L.seg_L : 0;
+  return KDA_OK;
+}
+
 int kda_fwd_intra(const kda_fwd_args* a) {
   kda::Params p;
   int st = check_call(a, NEED_INTRA, &p);

@@ -24,7 +24,7 @@ KDA_FLAG_BETA_LOGITS = 1
 KDA_FLAG_STATE_BF16 = 2
 KDA_FLAG_CKPT_BF16 = 4
 
-EXPORTED = ("kda_fwd_workspace_bytes", "kda_fwd", "kda_fwd_intra", "kda_fwd_inter",
+EXPORTED = ("kda_fwd_workspace_bytes", "kda_fwd_scan_plan", "kda_fwd", "kda_fwd_intra", "kda_fwd_inter",
             "kda_debug_unpack", "kda_bwd_dhu_workspace_bytes", "kda_bwd_dhu", "kda_strerror")
 
 
@@ -79,6 +79,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         getattr(lib, name).argtypes = [P]
         getattr(lib, name).restype = c_int
     lib.kda_fwd_workspace_bytes.restype = c_int
+    lib.kda_fwd_scan_plan.argtypes = [P, ctypes.POINTER(ctypes.c_int32)]
+    lib.kda_fwd_scan_plan.restype = c_int
     lib.kda_debug_unpack.argtypes = [P] + [c_void_p] * 6
     lib.kda_debug_unpack.restype = c_int
     PB = ctypes.POINTER(KdaBwdDhuArgs)
@@ -139,6 +141,16 @@ def make_args(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, o=None, ht
     a.hc = _ptr(hc)
     a.seg_chunks = int(seg_chunks)
     return a
+
+
+def kda_fwd_scan_plan(args: KdaFwdArgs) -> int:
+    """Segment length of the 64-column scan these arguments select, or 0 for the
+    16-column serial scan (host only)."""
+    n = ctypes.c_int32(0)
+    st = load_library().kda_fwd_scan_plan(ctypes.byref(args), ctypes.byref(n))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_fwd_scan_plan")
+    return n.value
 
 
 def kda_fwd_workspace_bytes(args: KdaFwdArgs) -> int:

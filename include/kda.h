@@ -118,6 +118,18 @@ typedef struct kda_fwd_args {
  * read.  Returns KDA_OK and *bytes, or an error status. */
 int kda_fwd_workspace_bytes(const kda_fwd_args* a, size_t* bytes);
 
+/* The state scan these arguments select (host only, launches nothing; reads the same
+ * fields as kda_fwd_workspace_bytes plus seg_chunks).  On KDA_OK, *seg_chunks is 0
+ * for the 16-column serial scan, else the segment length in chunks of the
+ * 64-column scan (a value >= every sequence's chunk count means one segment per
+ * sequence).  The choice depends on the device's compute-unit count: with more
+ * 64-column workgroups than compute units one segment per sequence; else, for
+ * sequences of 96 chunks or more (the mean for varlen), 2 to 8 segments so that
+ * the full pass fills the device in one round; else the serial scan when its
+ * workgroups fill at least half the device or sequences are shorter than 64
+ * chunks, and segments of max(8, chunks / 8) otherwise. */
+int kda_fwd_scan_plan(const kda_fwd_args* a, int32_t* seg_chunks);
+
 /* The whole chunked forward: o (and ht) from q, k, v, g, beta, h0 (kernel-fun
  * docstring; FlashKDA recurrence phases 3-6).  Equivalent to kda_fwd_intra
  * followed by kda_fwd_inter on the same stream. */

@@ -121,6 +121,23 @@ def test_workspace_bytes(lib):
     assert ws(args(seg_chunks=-1))[0] == K.KDA_ERR_INVALID_ARG
 
 
+def test_scan_plan(lib):
+    # the scan choice, host only (256 compute units when no device is seen)
+    plan = lambda **kw: K.kda_fwd_scan_plan(args(**kw))
+    assert plan(B=1, T=8192, HQK=32, HV=32) == 32                # 4 segments: the full pass in one round
+    assert plan(B=1, T=8192, HQK=48, HV=48) == 64                # 2 segments
+    assert plan(B=1, T=8192, HQK=16, HV=16) == 16                # 8 segments
+    assert plan(B=1, T=4096, HQK=32, HV=32) == 0                 # 64 chunks, 256 serial workgroups
+    assert plan(B=4, T=8192, HQK=32, HV=32, N=4) >= 128              # 256 wide workgroups: one segment each
+    assert plan(B=1, T=16384, HQK=2, HV=2) == 32                 # 8 segments
+    assert plan(B=1, T=8192, HQK=32, HV=32, seg_chunks=5) == 5   # forced
+    assert plan(B=1, T=200, HQK=1, HV=1) == 0
+    n = ctypes.c_int32(0)
+    assert lib.kda_fwd_scan_plan(None, ctypes.byref(n)) == K.KDA_ERR_INVALID_ARG
+    assert lib.kda_fwd_scan_plan(ctypes.byref(args()), None) == K.KDA_ERR_INVALID_ARG
+    assert lib.kda_fwd_scan_plan(ctypes.byref(args(K=96)), ctypes.byref(n)) == K.KDA_ERR_UNSUPPORTED
+
+
 ALL = ("kda_fwd", "kda_fwd_intra", "kda_fwd_inter")
 INTRA = ("kda_fwd", "kda_fwd_intra")     # entry points that read q, k, g, beta
 INTER = ("kda_fwd", "kda_fwd_inter")     # entry points that read v, o, h0, ht
