@@ -51,15 +51,15 @@ CFG_ID = 3
 METRIC = "KDA fwd tokens/s at T=8192,H=32,K=V=128 bf16; % of HBM/MFMA roofline"
 FLOPS_PER_TOKEN_HEAD = 180224
 # Sources whose change invalidates a kernel's committed counter figures.  The scan
-# kernels include the host file that chooses between them (a figure taken on one
+# kernels include the host header that chooses between them (a figure taken on one
 # scan must not be reported for a call that now runs the other).
 _CS = "gated_delta_rule_chunked_amd/csrc/"
 KERNEL_SOURCES = {
     "intra": [_CS + "kda_intra.hip", _CS + "kda_device.hpp"],
-    "inter": [_CS + "kda_inter.hip", _CS + "kda_device.hpp", _CS + "kda_api.cpp"],
+    "inter": [_CS + "kda_inter.hip", _CS + "kda_device.hpp", _CS + "kda_plan.hpp"],
     "bwd_dhu": [_CS + "kda_bwd.hip", _CS + "kda_device.hpp"],
-    "scan_state": [_CS + "kda_scan.hip", _CS + "kda_device.hpp", _CS + "kda_api.cpp"],
-    "scan_full": [_CS + "kda_scan.hip", _CS + "kda_device.hpp", _CS + "kda_api.cpp"],
+    "scan_state": [_CS + "kda_scan.hip", _CS + "kda_device.hpp", _CS + "kda_plan.hpp"],
+    "scan_full": [_CS + "kda_scan.hip", _CS + "kda_device.hpp", _CS + "kda_plan.hpp"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hip_runtime_api.h

@@ -11,6 +11,7 @@
 #include "../../include/kda.h"
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
+#include "kda_plan.hpp"
 
 static_assert(offsetof(kda_fwd_args, scale) == 40 && offsetof(kda_fwd_args, B) == 64 &&
                   offsetof(kda_fwd_args, o) == 96 && offsetof(kda_fwd_args, stream) == 128 &&
@@ -69,32 +70,10 @@ int check_shapes(const kda_fwd_args* a, kda::WsLayout* L) {
   if (units16 >= ((int64_t)1 << 31) - 8) return KDA_ERR_INVALID_ARG;
   if (a->N >= (1 << 30)) return KDA_ERR_INVALID_ARG;
   // scan choice and segment plan
-  bool seg_path;
-  int64_t seg_L;
-  if (a->seg_chunks > 0) {
-    seg_path = true;
-    seg_L = a->seg_chunks;
-  } else {
-    const int64_t cus = kda::device_cus();
-    const int64_t units64 = (int64_t)a->N * a->HV * ((a->V + 63) / 64);
-    // chunks per sequence (the mean for varlen, where the lengths stay on the device)
-    const int64_t per_seq = a->cu_seqlens ? nt / std::max<int64_t>(a->N, 1) : nt;
-    if (units64 >= cus) {            // 64-column workgroups alone fill the device: one segment each
-      seg_path = true;
-      seg_L = std::max<int64_t>(nt, 1);
-    } else if (per_seq >= 96) {
-      // long sequences: as many segments per sequence (2 to 8) as one round of the
-      // full pass's 64-column workgroups allows; measured at or faster than the
-      // 16-column serial scan from 16 to 64 heads at 6,144 to 32,768 tokens (at 4,096
-      // tokens the two are even)
-      seg_path = true;
-      const int64_t S = std::min<int64_t>(8, std::max<int64_t>(2, cus / units64));
-      seg_L = (per_seq + S - 1) / S;
-    } else {
-      seg_path = units16 * 2 < cus && nt >= 64;
-      seg_L = std::max<int64_t>(8, (nt + 7) / 8);
-    }
-  }
+  const kda::ScanPlan plan = kda::choose_scan(nt, a->cu_seqlens != nullptr, a->N, a->HV, a->V,
+                                              a->seg_chunks > 0 ? 0 : kda::device_cus(), a->seg_chunks);
+  const bool seg_path = plan.seg_path;
+  int64_t seg_L = plan.seg_L;
   seg_L = std::min<int64_t>(seg_L, std::max<int64_t>(nt, 1));
   int64_t seg_S = 1, max_segs = 0;
   bool multi = false;
