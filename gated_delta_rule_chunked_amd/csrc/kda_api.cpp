@@ -38,16 +38,8 @@ int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
 
 // Shape checks shared by every entry point.  Fills the layout on success.
 //
-// Choice of scan (kda_inter.hip or kda_scan.hip).  The 64-column workgroups of
-// kda_scan.hip stream a chunk's record once for four times the columns of the
-// 16-column workgroups of kda_inter.hip, so they are used whenever they alone fill
-// the compute units (every sequence is then one segment).  Otherwise the 16-column
-// scan is used when it has a workgroup for at least every other compute unit, or
-// when sequences are short; and else the segmented scan cuts each sequence into
-// segments of L chunks joined through the scan's affine dependence on its start
-// state, with L = max(8, ceil(chunks / 8)) (at most eight segments per sequence:
-// the full pass joins segment s through s - 1 small products).  A positive
-// seg_chunks selects kda_scan.hip with that L.
+// Choice of scan (kda_inter.hip or kda_scan.hip): kda_plan.hpp.  A positive
+// seg_chunks selects kda_scan.hip with that segment length.
 int check_shapes(const kda_fwd_args* a, kda::WsLayout* L) {
   if (!a) return KDA_ERR_INVALID_ARG;
   if (a->K != 64 && a->K != 128) return KDA_ERR_UNSUPPORTED;

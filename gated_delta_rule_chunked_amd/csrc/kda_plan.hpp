@@ -26,7 +26,7 @@ inline ScanPlan choose_scan(int64_t nt, bool varlen, int64_t n_seq, int64_t hv, 
                             int64_t forced) {
   if (forced > 0) return {true, forced};
   const int64_t units16 = n_seq * hv * (v / 16);           // 16-column workgroups
-  const int64_t units64 = n_seq * hv * ((v + 63) / 64);    // 64-column workgroups per segment round
+  const int64_t units64 = std::max<int64_t>(1, n_seq * hv * ((v + 63) / 64));   // per segment round
   // chunks per sequence (the mean for varlen, where the lengths stay on the device)
   const int64_t per_seq = varlen ? nt / std::max<int64_t>(n_seq, 1) : nt;
   if (units64 >= cus)   // 64-column workgroups alone fill the device: one segment each
