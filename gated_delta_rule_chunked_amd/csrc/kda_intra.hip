@@ -28,7 +28,8 @@
 // record layout.  Results leave the MFMA C layout directly as record fragments:
 // Aqk is computed transposed (operands swapped) and w as w^T = kd^T TmB^T, so a
 // lane's accumulator pair already is its P-order fragment; only kg^T and kd^T
-// (contractions over tokens) are transposed through LDS.
+// (contractions over tokens) are transposed through LDS: written row-major, read
+// back with the gfx950 transpose read.
 
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
@@ -40,24 +41,19 @@ namespace kda {
 template <int K>
 struct IntraSmem {
   static constexpr int S = K / 32;
-  static constexpr int TS = 72;                         // transposed-tile row stride (bf16)
+  static constexpr int RS = K + 16;                     // row-major [64][K] tile row stride (bf16)
   static constexpr int TOT = 0;                         // float [4][K] block gate totals
   static constexpr int TAB = TOT + 4 * K * 4;           // float [14][K] E, F, c tables
   static constexpr int BETA = TAB + 14 * K * 4;         // float [64]
   static constexpr int KY = BETA + 256;                 // float [3][S][64][8] k*Y, blocks 0..2
   static constexpr int KY_BYTES = 3 * S * 64 * 8 * 4;
-  static constexpr int KT = KY + KY_BYTES;              // bf16 [K][TS]: kg^T, later (k exp(Gam))^T
-  static constexpr int END0 = KT + K * TS * 2;
+  static constexpr int KT = KY + KY_BYTES;              // bf16 [64][RS]: kg, later k exp(Gam)
+  static constexpr int END0 = KT + 64 * RS * 2;
   static constexpr int AS = 68;                         // Akk / Tm row stride (fp32)
   static constexpr int AKK_BYTES = 64 * AS * 4;
   static constexpr int AKK = (KY_BYTES >= AKK_BYTES) ? KY : END0;   // reuses k*Y when it fits
   static constexpr int BYTES = (AKK == KY) ? END0 : END0 + AKK_BYTES;
 };
-
-// Row of the transposed [K][64] tiles: 8-token groups are XOR-swizzled by
-// (d >> 3) & 3 on bits 4-5 so that the column writes of a wave spread over the
-// LDS banks while every 8-token group stays contiguous (16-byte reads).
-__device__ __forceinline__ int tcol(int t, int d) { return t ^ (((d >> 3) & 3) << 4); }
 
 struct ChunkLoc {
   int b;
@@ -318,11 +314,18 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
   }
   __syncthreads();  // B2: tables
 
-  // Transposed [K][TS] tile address of (key dim d, this lane's row i): for the
-  // P-order dims d = 32s + 4g + e (lo half) and 32s + 16 + 4g + e (hi half) the
-  // swizzle depends only on g and the half, so two lane bases plus a constant.
-  const int kt_lo = (4 * g) * SM::TS + tcol(i, 4 * g);
-  const int kt_hi = (16 + 4 * g) * SM::TS + tcol(i, 16 + 4 * g);
+  // Row-major [64][K] tile of kg (later of k exp(Gam)): lane (g, r) writes row i at
+  // its P-order dims, 8 bytes at a time.  The row stride of K + 16 elements starts
+  // eight consecutive rows on eight different groups of 8 banks.
+  uint8_t* const kt_row = reinterpret_cast<uint8_t*>(sKT) + (i * SM::RS + 4 * g) * 2;   // row i, dims 4g..
+  // transpose-read lane address: lane (b, j, a) reads row 4b + j, columns 4a..4a+3
+  const uint8_t* const kt_tr = reinterpret_cast<const uint8_t*>(sKT) +
+                               ((4 * (ln >> 4) + ((ln >> 2) & 3)) * SM::RS + 4 * (ln & 3)) * 2;
+  auto kt_frag = [&](int tok0, int dim0) {   // P-order fragment of the transpose: dims dim0.., tokens tok0..
+    const uint2 lo = lds_tr8(kt_tr + (tok0 * SM::RS + dim0) * 2);
+    const uint2 hi = lds_tr8(kt_tr + ((tok0 + 16) * SM::RS + dim0) * 2);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  };
   bf16x8 QX[S], KX[S], KYr[S];
   uint4 KD[S];
 #pragma unroll
@@ -334,7 +337,7 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
       const uint2 kw = hf ? make_uint2(uks[s].z, uks[s].w) : make_uint2(uks[s].x, uks[s].y);
       const float qf[4] = {bflo(qw.x), bfhi(qw.x), bflo(qw.y), bfhi(qw.y)};
       const float kf[4] = {bflo(kw.x), bfhi(kw.x), bflo(kw.y), bfhi(kw.y)};
-      float qx[4], kx[4], ky[4], qg[4], kd[4];
+      float qx[4], kx[4], ky[4], qg[4], kd[4], kgv[4];
       const int d0 = 32 * s + 16 * hf + 4 * g;   // 4 consecutive key dims
       const float4 tot4 = *reinterpret_cast<const float4*>(sTot + I * K + d0);
       const float4 E4 = *reinterpret_cast<const float4*>(sTab + I * K + d0);
@@ -352,13 +355,15 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
         ky[e] = kf[e] * Y;
         qg[e] = p.scale * qx[e] * Ev[e];
         kd[e] = kx[e] * Ev[e];
-        sKT[(hf ? kt_hi : kt_lo) + (32 * s + e) * SM::TS] = f2bf(ky[e] * Fv[e]);   // kg^T
+        kgv[e] = ky[e] * Fv[e];
       }
       pq[hf] = make_uint2(pack2(qx[0], qx[1]), pack2(qx[2], qx[3]));
       pk[hf] = make_uint2(pack2(kx[0], kx[1]), pack2(kx[2], kx[3]));
       py[hf] = make_uint2(pack2(ky[0], ky[1]), pack2(ky[2], ky[3]));
       pg[hf] = make_uint2(pack2(qg[0], qg[1]), pack2(qg[2], qg[3]));
       pd[hf] = make_uint2(pack2(kd[0], kd[1]), pack2(kd[2], kd[3]));
+      *reinterpret_cast<uint2*>(kt_row + (32 * s + 16 * hf) * 2) =
+          make_uint2(pack2(kgv[0], kgv[1]), pack2(kgv[2], kgv[3]));   // kg, row-major
       if (I < 3)
         reinterpret_cast<float4*>(sKY + ((I * S + s) * 64 + ln) * 8)[hf] = make_float4(ky[0], ky[1], ky[2], ky[3]);
     }
@@ -373,11 +378,7 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
   // ---- phase 2: kg^T record; (k exp(Gam))^T; transposed Aqk / Akk of block row I --
   for (int f = I; f < 2 * (K / 16); f += 4) {
     const int md = f >> 1, s2 = f & 1;
-    const int d = 16 * md + r;
-    const uint16_t* row = sKT + d * SM::TS;
-    const uint2 lo = *reinterpret_cast<const uint2*>(row + tcol(32 * s2 + 4 * g, d));
-    const uint2 hi = *reinterpret_cast<const uint2*>(row + tcol(32 * s2 + 16 + 4 * g, d));
-    store_stream(rec + R::KGT + (f * 64 + ln) * 16, make_uint4(lo.x, lo.y, hi.x, hi.y));
+    store_stream(rec + R::KGT + (f * 64 + ln) * 16, kt_frag(32 * s2, 16 * md));
   }
   __syncthreads();  // B4: every read of kg^T is done
   // The next item's inputs load in three parts spread over phases 2-3 (g here, q
@@ -385,13 +386,9 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
   // for queue space behind this item's record stores.
   fetch_part(next, next_row, next_len, 2);   // g and beta of the next item
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const uint32_t wd[4] = {KD[s].x, KD[s].y, KD[s].z, KD[s].w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint16_t v = (uint16_t)((wd[e >> 1] >> (16 * (e & 1))) & 0xffff);
-      sKT[(e < 4 ? kt_lo : kt_hi) + (32 * s + (e & 3)) * SM::TS] = v;   // (k exp(Gam))^T
-    }
+  for (int s = 0; s < S; ++s) {   // k exp(Gam), row-major
+    *reinterpret_cast<uint2*>(kt_row + (32 * s) * 2) = make_uint2(KD[s].x, KD[s].y);
+    *reinterpret_cast<uint2*>(kt_row + (32 * s + 16) * 2) = make_uint2(KD[s].z, KD[s].w);
   }
   // C = (k Y c) (q X)^T: lane holds [j = 16J + 4g + rr][i = 16I + r], i.e. row i of
   // Aqk / Akk at columns 16J + 4g + rr -- already the P-order A fragment of the
@@ -433,7 +430,7 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
       for (int rr = 0; rr < 4; ++rr) {
         const int j = 4 * g + rr;   // column within block J
         vq[h][rr] = (J < I || (J == I && j <= r)) ? p.scale * aq[rr] : 0.f;
-        vk[J][rr] = (J < I || (J == I && j < r)) ? bt * ak[rr] : 0.f;
+        vk[J][rr] = (J < I || (J == I && j < r)) ? -bt * ak[rr] : 0.f;   // -Akk
       }
     }
     if (s2 < tri_steps(I))
@@ -454,6 +451,10 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
   //     operand of X and the C layout of Y the B operand of Y, so a product needs
   //     X^T and Y in C layout and returns X Y in C layout.  The powers of N
   //     commute with the partial products, which are built as D <- D + N^(2^j) D.
+  //     The Akk blocks sit in LDS negated (the sign rides on beta when they leave
+  //     the accumulators): the first factor I - N is then I plus the stored block,
+  //     the even powers do not see the sign, and in 3b the minus of the recursion
+  //     is already in the stored A_MP.
   {
     auto mm = [&](const f32x4& xt, const f32x4& y) {
       f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -474,7 +475,7 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
     const f32x4 N8T = mm(N4, N4T);
     f32x4 D;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) D[e] = (4 * g + e == r ? 1.f : 0.f) - N[e];
+    for (int e = 0; e < 4; ++e) D[e] = (4 * g + e == r ? 1.f : 0.f) + N[e];   // N holds -Akk
     D += mm(N2T, D);
     D += mm(N4T, D);
     D += mm(N8T, D);
@@ -515,7 +516,7 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
         const float a = sAkk[(16 * M + r) * SM::AS + 16 * M + 4 * g + kb];
         D = mfma16x4f32(a, P[kb], D);
       }
-      inv[M] = -D;
+      inv[M] = D;   // the Akk blocks are stored negated
     }
   }
   __syncthreads();  // B8: every read of the Akk blocks is done
@@ -528,7 +529,7 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
   __syncthreads();  // B9: Tm complete
 
   // ---- phase 4: TmB = Tm diag(beta) fragments; w^T = (k exp(Gam))^T TmB^T ----------
-  bf16x8 TB[2];
+  bf16x8 TBn[2];   // -TmB: the w products then leave -w, the WN record, directly
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2) {
     if (s2 >= tri_steps(I)) continue;
@@ -541,7 +542,7 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
     const float t[8] = {t0.x * b0.x, t0.y * b0.y, t0.z * b0.z, t0.w * b0.w,
                         t1.x * b1.x, t1.y * b1.y, t1.z * b1.z, t1.w * b1.w};
     const uint4 u = pack8(t);
-    TB[s2] = as_frag(u);
+    TBn[s2] = as_frag(make_uint4(u.x ^ 0x80008000u, u.y ^ 0x80008000u, u.z ^ 0x80008000u, u.w ^ 0x80008000u));
     store_stream(rec + R::TMB + (tri_frag(I, s2) * 64 + ln) * 16, u);
   }
   // C[d][t] = sum_t' kd[t'][d] TmB[t][t'] = w[t][d]: lane holds w row 16I + r at
@@ -551,18 +552,14 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
     f32x4 acc[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int d = 16 * (2 * s + h) + r;
       acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         if (s2 >= tri_steps(I)) continue;
-        const uint16_t* row = sKT + d * SM::TS;
-        const uint2 lo = *reinterpret_cast<const uint2*>(row + tcol(32 * s2 + 4 * g, d));
-        const uint2 hi = *reinterpret_cast<const uint2*>(row + tcol(32 * s2 + 16 + 4 * g, d));
-        acc[h] = mfma16x32(as_frag(make_uint4(lo.x, lo.y, hi.x, hi.y)), TB[s2], acc[h]);
+        acc[h] = mfma16x32(as_frag(kt_frag(32 * s2, 16 * (2 * s + h))), TBn[s2], acc[h]);
       }
     }
-    store_stream(rec + R::WN + ((I * S + s) * 64 + ln) * 16, pack_pair(-acc[0], -acc[1]));
+    store_stream(rec + R::WN + ((I * S + s) * 64 + ln) * 16, pack_pair(acc[0], acc[1]));
   }
   draw_ticket();     // ticket (and location) for the item after next
   __syncthreads();  // B10: phase-4 reads of Tm, beta and (k exp(Gam))^T are done; s_next visible
