@@ -36,7 +36,9 @@
 //   waves 4-7 (loader waves): keep three chunks of records in flight in a register
 //     ring (1 KiB steps of the record, steps lw, lw+4, ...) together with 16 rows
 //     of the group's v columns, and copy chunk c+1 into the free slot of a
-//     two-slot LDS ring during chunk c.
+//     two-slot LDS ring during chunk c.  The rest of each record (the o operands in
+//     the full pass, half of the state part in the state pass) goes into that slot
+//     directly, by LDS-DMA loads issued as chunk c starts.
 
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
@@ -52,7 +54,16 @@ struct ScanSmem {
   using R = Rec<K>;
   // the full pass copies whole records, the state pass only their state part
   static constexpr int NSTEP = ((MODE == SCAN_FULL ? R::BYTES : R::STATE_BYTES) + 1023) / 1024;
-  static constexpr int NLD = (NSTEP + 3) / 4;        // steps per loader wave (the last ones repeat)
+  // The first NREG 1 KiB steps of a chunk go through the loaders' register ring
+  // (issued two phases ahead), the others straight into LDS with LDS-DMA loads
+  // (issued one phase ahead, into the slot the column waves have just released).
+  // Full pass: the state part by the ring, the o part (QG, AQK) by DMA; state pass:
+  // about half of the state part each way.  Interleaved A/B timing found these
+  // splits best (the whole record by DMA was slower: one phase is too little time
+  // for all of it to arrive).
+  static constexpr int NREG = MODE == SCAN_FULL ? (R::STATE_BYTES + 1023) / 1024 : (NSTEP + 1) / 2;
+  static constexpr int NLD = (NREG + 3) / 4;         // ring steps per loader wave (the last ones repeat)
+  static constexpr int NLDD = (NSTEP - NREG + 3) / 4;   // DMA steps per loader wave
   static constexpr int SLOT = NSTEP * 1024;
   static constexpr int VT = 2 * SLOT;                // v tiles: [2 slots][4 column waves][64][16] bf16
   static constexpr int VT_BYTES = BT * BV * 2;
@@ -151,7 +162,7 @@ __device__ __forceinline__ void scan_body(const Params& p, uint8_t* smem, const 
       const int c = chunk_of(ph);
       const uint8_t* rec = p.recs + rec_index(hv, sl.cbase + c, p.max_chunks) * (int64_t)R::BYTES + ln * 16;
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) dst[i] = *reinterpret_cast<const u32x4*>(rec + min(4 * i + lw, SM::NSTEP - 1) * 1024);
+      for (int i = 0; i < NLD; ++i) dst[i] = *reinterpret_cast<const u32x4*>(rec + min(4 * i + lw, SM::NREG - 1) * 1024);
       if (MODE != SCAN_M) {
         const int rbase = c * BT + 16 * lw + (ln >> 3);
         const int64_t t0 = row0 + min(rbase, sl.len - 1), t1 = row0 + min(rbase + 8, sl.len - 1);
@@ -162,7 +173,7 @@ __device__ __forceinline__ void scan_body(const Params& p, uint8_t* smem, const 
     auto put = [&](int ph, const u32x4* src, const uint4& v0, const uint4& v1) {
       uint8_t* slot = smem + (ph & 1) * SM::SLOT + ln * 16;
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) *reinterpret_cast<u32x4*>(slot + min(4 * i + lw, SM::NSTEP - 1) * 1024) = src[i];
+      for (int i = 0; i < NLD; ++i) *reinterpret_cast<u32x4*>(slot + min(4 * i + lw, SM::NREG - 1) * 1024) = src[i];
       if (MODE != SCAN_M) {
         const int row = 16 * lw + (ln >> 3);
         const int cb = chunk_of(ph) * BT;                       // rows past the sequence are zero
@@ -171,28 +182,65 @@ __device__ __forceinline__ void scan_body(const Params& p, uint8_t* smem, const 
         *reinterpret_cast<uint4*>(vt + 8 * 32) = cb + row + 8 < sl.len ? v1 : make_uint4(0, 0, 0, 0);
       }
     };
+    // steps NREG.. of chunk ph straight into slot ph & 1 (LDS-DMA: lane ln's 16 bytes
+    // land at the step's base + 16 ln, the record's own layout)
+    auto dma = [&](int ph) {
+      if (SM::NLDD == 0) return;
+      const int c = chunk_of(ph);
+      const uint8_t* rec = p.recs + rec_index(hv, sl.cbase + c, p.max_chunks) * (int64_t)R::BYTES + ln * 16;
+      uint8_t* slot = smem + (ph & 1) * SM::SLOT;
+#pragma unroll
+      for (int i = 0; i < SM::NLDD; ++i) {
+        const int st = min(SM::NREG + 4 * i + lw, SM::NSTEP - 1);   // the last steps repeat
+        // written as assembly so that the compiler's wait counting does not treat the
+        // LDS writes of the copy as aliasing every later LDS store of the wave (it then
+        // waits for all loads in flight, the ring's included); its own waits only come
+        // out more conservative for not counting these loads
+        const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(slot + st * 1024);
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(rec + st * 1024), "s"(lds) : "memory", "m0");
+      }
+    };
+    // Before a barrier the loader waits until only the ring loads issued after the
+    // phase's DMA are outstanding: the DMA data is then in LDS for the column waves.
+    constexpr int NAFTER = NLD + (MODE != SCAN_M ? 2 : 0);
+    static_assert(NAFTER <= 63, "fits the vmcnt counter");
+    auto wait_dma = [&]() {
+      if (SM::NLDD > 0) __builtin_amdgcn_s_waitcnt((NAFTER & 15) | ((NAFTER >> 4) << 14) | (7 << 4) | (15 << 8));
+    };
     u32x4 ra[NLD], rb[NLD], rc[NLD];
     uint4 va0, va1, vb0, vb1, vc0, vc1;
+    dma(0);
+    __builtin_amdgcn_sched_barrier(0);
     fetch(0, ra, va0, va1);
     fetch(1, rb, vb0, vb1);
     fetch(2, rc, vc0, vc1);
-    put(0, ra, va0, va1);
+    put(0, ra, va0, va1);   // waits for chunk 0's ring loads, and so for the older DMA
     barrier_lds();  // S0: chunk 0 of the segment in slot 0
     static_assert(SCAN_RING == 3, "the ring turn below is written out for three slots");
     for (int t0 = 0; t0 < nphase; t0 += SCAN_RING) {
+      dma(t0 + 1);
+      __builtin_amdgcn_sched_barrier(0);
       fetch(t0 + 3, ra, va0, va1);
       __builtin_amdgcn_sched_barrier(0);   // loads issue before the LDS writes
       put(t0 + 1, rb, vb0, vb1);
+      wait_dma();
       barrier_lds();
+      dma(t0 + 2);
+      __builtin_amdgcn_sched_barrier(0);
       fetch(t0 + 4, rb, vb0, vb1);
       __builtin_amdgcn_sched_barrier(0);
       put(t0 + 2, rc, vc0, vc1);
+      wait_dma();
       barrier_lds();
+      dma(t0 + 3);
+      __builtin_amdgcn_sched_barrier(0);
       fetch(t0 + 5, rc, vc0, vc1);
       __builtin_amdgcn_sched_barrier(0);
       put(t0 + 3, ra, va0, va1);
+      wait_dma();
       barrier_lds();
     }
+    __builtin_amdgcn_s_waitcnt(0);   // no LDS-DMA write may land after the workgroup ends
     return;
   }
 
