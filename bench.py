@@ -308,14 +308,16 @@ def main():
     torch.cuda.synchronize()
     copy_gbs = 5 * 2 * calib_src.numel() / (cev.ms(0, 1) * 1e-3) / 1e9
 
-    # cold-cache steps: a 1 GiB buffer written between steps evicts L2 and MALL
+    # cold-cache steps: a 1 GiB buffer read between steps evicts L2 and MALL.  It is
+    # read, not written: a write would leave the caches full of dirty lines whose
+    # write-back the timed step would then pay.
     cold_ms = None
     if args.cold:
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        flush = torch.ones(1 << 27, dtype=torch.int64, device=dev)
         cold = []
         cev = HipEvents(2)
         for _ in range(args.cold):
-            flush.fill_(1)
+            flush.sum()
             cev.record(0, stream)
             step()
             cev.record(1, stream)
