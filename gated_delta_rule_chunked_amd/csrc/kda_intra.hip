@@ -151,6 +151,20 @@ __global__ void prep_kernel(Params p) {
 }
 
 // ------------------------------------------------------------ intra kernel
+// Lowest per-token gate (natural log), -11, that the gate factoring takes: the factors of a
+// 16-row block are bounded by exp(8 |g|) = exp(88), finite in fp32 and bf16.  Lower
+// gates are raised to it.  That changes the decay of such a token from exp(g) to
+// exp(-11) ~ 1.7e-5, i.e. by at most 1.7e-5 of the state it multiplies, well below
+// the bf16 resolution of the outputs.  The floor is applied to the packed bf16 bits:
+// a negative bf16 value of larger magnitude has a larger unsigned 16-bit pattern,
+// positive values lie below 0x8000, so one unsigned 16-bit min per pair does it
+// (-inf, 0xff80, becomes -11; so does a NaN with its sign bit set).
+constexpr uint16_t GATE_MIN_BF16 = 0xc130;   // -11.0
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t gate_floor2(uint32_t w) {
+  const u16x2 lim = {GATE_MIN_BF16, GATE_MIN_BF16};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, w), lim));
+}
 #ifndef KDA_INTRA_OCC
 #define KDA_INTRA_OCC 2   // workgroups per CU the register budget is sized for
 #endif
@@ -265,7 +279,7 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
   for (int s = 0; s < S; ++s) {
     uqs[s] = nq[s];
     uks[s] = nk[s];
-    unpack8(ng[s], gl[s]);
+    unpack8(make_uint4(gate_floor2(ng[s].x), gate_floor2(ng[s].y), gate_floor2(ng[s].z), gate_floor2(ng[s].w)), gl[s]);
   }
   bt = bf2f((uint16_t)nb);
   if (p.flags & FLAG_BETA_LOGITS)   // FlashKDA's fused sigmoid: 1 / (1 + e^-x), exact 0 and 1 at -inf, +inf

@@ -61,7 +61,10 @@ typedef struct kda_fwd_args {
   /* Inputs (device, bf16 unless stated).
    *   q, k : [B, T, HQK, K]  keys/queries, expected L2-normalised over K by the caller
    *   v    : [B, T, HV,  V]
-   *   g    : [B, T, HV,  K]  natural-log per-dimension decay, g <= 0
+   *   g    : [B, T, HV,  K]  natural-log per-dimension decay, g <= 0; values
+   *          below -11, -inf included, are taken as -11 (a decay of 1.7e-5
+   *          instead of a smaller one: the outputs change by at most 1.7e-5 of the
+   *          state it multiplies); so is a NaN with its sign bit set
    *   beta : [B, T, HV]      write strength in [0, 1] (already through a sigmoid),
    *          or its logit with KDA_FLAG_BETA_LOGITS
    *   h0   : [N, HV, K, V] initial state per sequence and value head, fp32 (bf16

@@ -112,6 +112,23 @@ def test_strong_decay_stays_finite():
     check(o, ht, *full_oracle(d))
 
 
+def test_gates_below_the_supported_range():
+    # gates below -11 (here -30, -1000 and -inf on whole tokens and on single
+    # dimensions) are raised to -11 in the intra stage; the outputs stay finite and
+    # within the tolerance of the exact recurrence, which decays those tokens fully
+    d = make_inputs(43, B=1, T=200, HQK=1, HV=2, K=128, V=64, has_h0=True)
+    g = d["g"]
+    g[0, 5, 0, :] = -30.0
+    g[0, 63, 1, :] = -1000.0
+    g[0, 64, 0, :] = -np.inf
+    g[0, 70:90, 1, 3] = -np.inf
+    g[0, 100:140:7, :, 17] = -30.0
+    g[0, 199, :, :] = -np.inf
+    o, ht = run_hip(d)
+    assert np.isfinite(o).all() and np.isfinite(ht).all()
+    check(o, ht, *full_oracle(d))
+
+
 def test_intermediates_match_chunked_oracle():
     """The intra stage alone: qg, w, kg, Aqk, Tm diag(beta), exp(G) against the
     chunked oracle's per-chunk intermediates."""
