@@ -219,8 +219,8 @@ __device__ __host__ __forceinline__ constexpr int tri_steps(int mb) { return mb 
 // chunk_base[N+1]) and an int32 error flag from byte 16, then (segmented scan) the
 // segment table (int32 seg_base[N+1]) and, 8-byte aligned, int32 {first row, valid
 // rows} per chunk; padded to a multiple of 256 bytes.  The pad keeps the scan's
-// whole-KiB record copies inside the workspace.  B (fp32 [segments, HV, K, V]) and
-// M (bf16 [segments, HV, K, K]) hold the segmented scan's per-segment end states and
+// whole-KiB record copies inside the workspace.  B (fp32, K x V per segment and HV) and
+// M (bf16, K x K per segment and HV) hold the segmented scan's per-segment end states and
 // transitions; they are empty when no sequence has more than one segment.
 struct WsLayout {
   int64_t table_bytes;  // header: counter, varlen chunk table, segment table and chunk info

@@ -39,8 +39,10 @@ struct Params {
   int seg_S;             // fixed length: segments per sequence
   int64_t max_segs;      // capacity of the segment buffers (segments over all sequences)
   int32_t* segtab;       // varlen: seg_base[N+1] in the workspace header, else nullptr
-  float* bbuf;           // [max_segs, HV, K, V] fp32 segment end states, or nullptr (one segment)
-  uint16_t* mbuf;        // [max_segs, HV, K, K] bf16 segment transitions, or nullptr
+  float* bbuf;           // K x V fp32 segment end states per (segment, HV), in the column
+                         // waves' C-layout order (kda_scan.hip), or nullptr (one segment)
+  uint16_t* mbuf;        // K x K bf16 segment transitions per (segment, HV), as P-order A
+                         // fragments (kda_scan.hip), or nullptr
 };
 
 // Reverse state scan of the backward (kda_bwd_dhu).

@@ -23,7 +23,8 @@
 //     h_s = M_{s-1} h_{s-1} + b_{s-1} formed in its prologue, and writes o (and the
 //     final state after the last segment).
 // b is kept in fp32, M in bf16 (it multiplies a bf16 copy of h on MFMA, as w does
-// within a chunk).
+// within a chunk); both in the register order the full pass's prologue loads them
+// in, so that its s - 1 products wait for one batch of whole-line loads each.
 //
 // Eight waves per workgroup, one barrier per chunk:
 //   waves 0-3 (column waves): wave c holds h for columns 16c..16c+15 of the group
@@ -268,30 +269,36 @@ __device__ __forceinline__ void scan_body(const Params& p, uint8_t* smem, const 
         h[md][rr] = from_h0 ? load_state(state_bf16, p.h0, (((int64_t)sl.n * p.HV + hv) * K + d) * p.V + col) : 0.f;
       }
   } else {
-    // full pass, s >= 1: h_1 = b_0, h_{s'+1} = M_{s'} h_{s'} + b_{s'}
+    // full pass, s >= 1: h_1 = b_0, h_{s'+1} = M_{s'} h_{s'} + b_{s'}.  b is stored in
+    // this wave's C-layout order and M as P-order A fragments (see the state pass's
+    // stores), so both arrive as whole 1 KiB wave loads; a hop's loads are all issued
+    // before its products.
     auto load_b = [&](int64_t sig, f32x4* x) {
-      const float* bb = p.bbuf + ((sig * p.HV + hv) * K) * (int64_t)p.V + col;
+      const float4* bb = reinterpret_cast<const float4*>(p.bbuf) +
+                         ((sig * p.HV + hv) * (p.V / BV) + col / BV) * (int64_t)(ND * 64) + ln;
 #pragma unroll
-      for (int md = 0; md < ND; ++md)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) x[md][rr] = bb[(int64_t)(16 * md + 4 * g + rr) * p.V];
+      for (int md = 0; md < ND; ++md) {
+        const float4 t = bb[md * 64];
+        x[md] = f32x4{t.x, t.y, t.z, t.w};
+      }
     };
     load_b(sl.sigma0, h);
     for (int s2 = 1; s2 < sl.s; ++s2) {
+      f32x4 hn[ND];
+      load_b(sl.sigma0 + s2, hn);
+      const uint4* Mf = reinterpret_cast<const uint4*>(p.mbuf + ((sl.sigma0 + s2) * p.HV + hv) * (int64_t)K * K) + ln;
+      uint4 mf[ND * S];
+#pragma unroll
+      for (int f = 0; f < ND * S; ++f) mf[f] = Mf[f * 64];
       uint2 hb[ND];
 #pragma unroll
       for (int md = 0; md < ND; ++md) hb[md] = pack4(h[md]);
-      f32x4 hn[ND];
-      load_b(sl.sigma0 + s2, hn);
-      const uint16_t* M = p.mbuf + ((sl.sigma0 + s2) * p.HV + hv) * (int64_t)K * K + r * K + 4 * g;
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int md = 0; md < ND; ++md)
 #pragma unroll
-        for (int s3 = 0; s3 < S; ++s3) {
-          const uint16_t* a = M + 16 * md * K + 32 * s3;
-          hn[md] = mfma16x32(cat(*reinterpret_cast<const uint2*>(a), *reinterpret_cast<const uint2*>(a + 16)),
-                             cat(hb[2 * s3], hb[2 * s3 + 1]), hn[md]);
-        }
+        for (int s3 = 0; s3 < S; ++s3)
+          hn[md] = mfma16x32(as_frag(mf[md * S + s3]), cat(hb[2 * s3], hb[2 * s3 + 1]), hn[md]);
 #pragma unroll
       for (int md = 0; md < ND; ++md) h[md] = hn[md];
     }
@@ -453,21 +460,21 @@ __device__ __forceinline__ void scan_body(const Params& p, uint8_t* smem, const 
   // the segment's end state (row strides made opaque, so that the 32 row offsets are
   // not computed ahead of the chunk loop and kept live through it)
   if (MODE == SCAN_B) {
-    int sv = p.V;
-    asm volatile("" : "+s"(sv));
-    float* bb = p.bbuf + ((sigma * p.HV + hv) * K + 4 * g) * (int64_t)sv + col;
+    // b in the C-layout order of this column tile: [segment][HV][V/16][K/16][64 lanes][4]
+    float4* bb = reinterpret_cast<float4*>(p.bbuf) + ((sigma * p.HV + hv) * (p.V / BV) + col / BV) * (int64_t)(ND * 64) + ln;
 #pragma unroll
-    for (int md = 0; md < ND; ++md)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) bb[(int64_t)(16 * md + rr) * sv] = h[md][rr];
+    for (int md = 0; md < ND; ++md) bb[md * 64] = make_float4(h[md][0], h[md][1], h[md][2], h[md][3]);
   } else if (MODE == SCAN_M) {
-    int sk = K;
-    asm volatile("" : "+s"(sk));
-    uint16_t* mm = p.mbuf + (sigma * p.HV + hv) * (int64_t)K * K + 4 * g * sk + col;
+    // M as P-order A fragments of the full pass's products M h: fragment (md, s3) holds
+    // rows 16 md.., columns 32 s3..; this lane's column col lands in lane group gp,
+    // element e, and its rows 16 md + 4 g + rr in lanes 16 gp + 4 g + rr
+    uint16_t* mm = p.mbuf + (sigma * p.HV + hv) * (int64_t)K * K;
+    const int s3 = col >> 5, q = col & 31;
+    const int gp = (q & 15) >> 2, e = (q & 3) + 4 * (q >> 4);
 #pragma unroll
     for (int md = 0; md < ND; ++md)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) mm[(16 * md + rr) * sk] = f2bf(h[md][rr]);
+      for (int rr = 0; rr < 4; ++rr) mm[((md * S + s3) * 64 + 16 * gp + 4 * g + rr) * 8 + e] = f2bf(h[md][rr]);
   } else if (p.ht && sl.s == sl.nseg - 1) {
 #pragma unroll
     for (int md = 0; md < ND; ++md)
