@@ -79,7 +79,7 @@ def test_varlen_workload_sampled():
 
 
 @pytest.mark.parametrize("T", [1, 17, 63, 64, 65, 200, 257])
-@pytest.mark.parametrize("K,V", [(128, 128), (64, 48)])
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 48), (128, 256), (64, 16)])
 def test_ragged_lengths(T, K, V):
     d = make_inputs(100 + T, B=2, T=T, HQK=1, HV=2, K=K, V=V, has_h0=True)
     o, ht = run_hip(d)

@@ -41,7 +41,7 @@ def reference(d, h0=None):
 
 
 @pytest.mark.parametrize("seg", [1, 2, 3, 8])
-@pytest.mark.parametrize("K,V", [(128, 64), (128, 48), (128, 80), (64, 128)])
+@pytest.mark.parametrize("K,V", [(128, 64), (128, 48), (128, 80), (64, 128), (128, 256), (64, 16)])
 def test_fixed_length_forced_segments(seg, K, V):
     d = make_inputs(131, B=2, T=64 * 7 + 13, HQK=2, HV=4, K=K, V=V, has_h0=True)
     o, ht = run(d, seg_chunks=seg)
