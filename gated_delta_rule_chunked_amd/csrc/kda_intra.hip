@@ -47,8 +47,9 @@ struct IntraSmem {
   static constexpr int BETA = TAB + 14 * K * 4;         // float [64]
   static constexpr int KY = BETA + 256;                 // float [3][S][64][8] k*Y, blocks 0..2
   static constexpr int KY_BYTES = 3 * S * 64 * 8 * 4;
-  static constexpr int KT = KY + KY_BYTES;              // bf16 [64][RS]: kg, later k exp(Gam)
-  static constexpr int END0 = KT + 64 * RS * 2;
+  static constexpr int KT = KY + KY_BYTES;              // bf16 [64][RS]: kg
+  static constexpr int KDT = KT + 64 * RS * 2;          // bf16 [64][RS]: k exp(Gam)
+  static constexpr int END0 = KDT + 64 * RS * 2;
   static constexpr int AS = 68;                         // Akk / Tm row stride (fp32)
   static constexpr int AKK_BYTES = 64 * AS * 4;
   static constexpr int AKK = (KY_BYTES >= AKK_BYTES) ? KY : END0;   // reuses k*Y when it fits
@@ -265,7 +266,7 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
   draw_ticket();
   __syncthreads();
   while (item < n_items) {
-  // written before the last barrier; rewritten only after B9
+  // written before the last barrier; rewritten only after B8
   const int next = __builtin_amdgcn_readfirstlane(s_next);
   const int64_t next_row = s_nrow;
   const int next_len = __builtin_amdgcn_readfirstlane(s_nlen);
@@ -328,16 +329,19 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
   }
   __syncthreads();  // B2: tables
 
-  // Row-major [64][K] tile of kg (later of k exp(Gam)): lane (g, r) writes row i at
-  // its P-order dims, 8 bytes at a time.  The row stride of K + 16 elements starts
+  // Row-major [64][K] tiles of kg and of k exp(Gam) (two tiles, so that writing the
+  // second needs no barrier after the reads of the first): lane (g, r) writes row i
+  // at its P-order dims, 8 bytes at a time.  The row stride of K + 16 elements starts
   // eight consecutive rows on eight different groups of 8 banks.
   uint8_t* const kt_row = reinterpret_cast<uint8_t*>(sKT) + (i * SM::RS + 4 * g) * 2;   // row i, dims 4g..
   // transpose-read lane address: lane (b, j, a) reads row 4b + j, columns 4a..4a+3
   const uint8_t* const kt_tr = reinterpret_cast<const uint8_t*>(sKT) +
                                ((4 * (ln >> 4) + ((ln >> 2) & 3)) * SM::RS + 4 * (ln & 3)) * 2;
-  auto kt_frag = [&](int tok0, int dim0) {   // P-order fragment of the transpose: dims dim0.., tokens tok0..
-    const uint2 lo = lds_tr8(kt_tr + (tok0 * SM::RS + dim0) * 2);
-    const uint2 hi = lds_tr8(kt_tr + ((tok0 + 16) * SM::RS + dim0) * 2);
+  // P-order fragment of the transpose of tile `tile` (byte offset from the kg tile):
+  // key dims dim0.., tokens tok0..
+  auto kt_frag = [&](int tok0, int dim0, int tile = 0) {
+    const uint2 lo = lds_tr8(kt_tr + tile + (tok0 * SM::RS + dim0) * 2);
+    const uint2 hi = lds_tr8(kt_tr + tile + ((tok0 + 16) * SM::RS + dim0) * 2);
     return make_uint4(lo.x, lo.y, hi.x, hi.y);
   };
   bf16x8 QX[S], KX[S], KYr[S];
@@ -394,15 +398,14 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
     const int md = f >> 1, s2 = f & 1;
     store_stream(rec + R::KGT + (f * 64 + ln) * 16, kt_frag(32 * s2, 16 * md));
   }
-  __syncthreads();  // B4: every read of kg^T is done
   // The next item's inputs load in three parts spread over phases 2-3 (g here, q
-  // after B6, k after B7): issued at once they waited about 6k cycles per item
+  // after B5, k after B6): issued at once they waited about 6k cycles per item
   // for queue space behind this item's record stores.
   fetch_part(next, next_row, next_len, 2);   // g and beta of the next item
 #pragma unroll
   for (int s = 0; s < S; ++s) {   // k exp(Gam), row-major
-    *reinterpret_cast<uint2*>(kt_row + (32 * s) * 2) = make_uint2(KD[s].x, KD[s].y);
-    *reinterpret_cast<uint2*>(kt_row + (32 * s + 16) * 2) = make_uint2(KD[s].z, KD[s].w);
+    *reinterpret_cast<uint2*>(kt_row + (SM::KDT - SM::KT) + (32 * s) * 2) = make_uint2(KD[s].x, KD[s].y);
+    *reinterpret_cast<uint2*>(kt_row + (SM::KDT - SM::KT) + (32 * s + 16) * 2) = make_uint2(KD[s].z, KD[s].w);
   }
   // C = (k Y c) (q X)^T: lane holds [j = 16J + 4g + rr][i = 16I + r], i.e. row i of
   // Aqk / Akk at columns 16J + 4g + rr -- already the P-order A fragment of the
@@ -450,11 +453,11 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
     if (s2 < tri_steps(I))
       store_stream(rec + R::AQK + (tri_frag(I, s2) * 64 + ln) * 16, pack_pair(vq[0], vq[1]));
   }
-  __syncthreads();  // B5: every read of k*Y is done (Akk reuses its space)
+  __syncthreads();  // B4: every read of k*Y is done (Akk reuses its space)
 #pragma unroll
   for (int J = 0; J < 4; ++J)
     *reinterpret_cast<float4*>(sAkk + i * SM::AS + 16 * J + 4 * g) = make_float4(vk[J][0], vk[J][1], vk[J][2], vk[J][3]);
-  __syncthreads();  // B6: Akk and (k exp(Gam))^T complete
+  __syncthreads();  // B5: Akk and (k exp(Gam))^T complete
   fetch_part(next, next_row, next_len, 0);   // q of the next item
 
   // ---- phase 3: Tm = (I + Akk)^-1 ------------------------------------------------
@@ -497,7 +500,7 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
 #pragma unroll
     for (int e = 0; e < 4; ++e) Aw[(4 * g + e) * SM::AS + r] = D[e];
   }
-  __syncthreads();  // B7: diagonal blocks hold D_I
+  __syncthreads();  // B6: diagonal blocks hold D_I
   fetch_part(next, next_row, next_len, 1);   // k of the next item
 
   // 3b: block column J = I below the diagonal:
@@ -533,14 +536,14 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
       inv[M] = D;   // the Akk blocks are stored negated
     }
   }
-  __syncthreads();  // B8: every read of the Akk blocks is done
+  __syncthreads();  // B7: every read of the Akk blocks is done
 #pragma unroll
   for (int M = 1; M < 4; ++M) {
     if (M <= I) continue;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) sAkk[(16 * M + 4 * g + rr) * SM::AS + 16 * I + r] = inv[M][rr];
   }
-  __syncthreads();  // B9: Tm complete
+  __syncthreads();  // B8: Tm complete
 
   // ---- phase 4: TmB = Tm diag(beta) fragments; w^T = (k exp(Gam))^T TmB^T ----------
   bf16x8 TBn[2];   // -TmB: the w products then leave -w, the WN record, directly
@@ -570,13 +573,13 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         if (s2 >= tri_steps(I)) continue;
-        acc[h] = mfma16x32(as_frag(kt_frag(32 * s2, 16 * (2 * s + h))), TBn[s2], acc[h]);
+        acc[h] = mfma16x32(as_frag(kt_frag(32 * s2, 16 * (2 * s + h), SM::KDT - SM::KT)), TBn[s2], acc[h]);
       }
     }
     store_stream(rec + R::WN + ((I * S + s) * 64 + ln) * 16, pack_pair(acc[0], acc[1]));
   }
   draw_ticket();     // ticket (and location) for the item after next
-  __syncthreads();  // B10: phase-4 reads of Tm, beta and (k exp(Gam))^T are done; s_next visible
+  __syncthreads();  // B9: phase-4 reads of Tm, beta and (k exp(Gam))^T are done; s_next visible
   item = next;
   cur_len = next_len;
   }
