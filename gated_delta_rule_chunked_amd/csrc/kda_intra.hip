@@ -49,7 +49,8 @@ struct IntraSmem {
   static constexpr int KY_BYTES = 3 * S * 64 * 8 * 4;
   static constexpr int KT = KY + KY_BYTES;              // bf16 [64][RS]: kg
   static constexpr int KDT = KT + 64 * RS * 2;          // bf16 [64][RS]: k exp(Gam)
-  static constexpr int END0 = KDT + 64 * RS * 2;
+  static constexpr int X3 = KDT + 64 * RS * 2;          // bf16 [2][S][64 lanes][8]: q X, k X of row block 3
+  static constexpr int END0 = X3 + 2 * S * 64 * 16;
   static constexpr int AS = 68;                         // Akk / Tm row stride (fp32)
   static constexpr int AKK_BYTES = 64 * AS * 4;
   static constexpr int AKK = (KY_BYTES >= AKK_BYTES) ? KY : END0;   // reuses k*Y when it fits
@@ -182,6 +183,7 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
   float* sBeta = reinterpret_cast<float*>(smem + SM::BETA);
   float* sKY = reinterpret_cast<float*>(smem + SM::KY);
   uint16_t* sKT = reinterpret_cast<uint16_t*>(smem + SM::KT);
+  uint4* sX3 = reinterpret_cast<uint4*>(smem + SM::X3);
   float* sAkk = reinterpret_cast<float*>(smem + SM::AKK);
 
   const int tid = threadIdx.x;
@@ -387,6 +389,10 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
     }
     QX[s] = as_frag(make_uint4(pq[0].x, pq[0].y, pq[1].x, pq[1].y));
     KX[s] = as_frag(make_uint4(pk[0].x, pk[0].y, pk[1].x, pk[1].y));
+    if (I == 3) {   // wave 0 computes row block 3's first Aqk / Akk fragment pair
+      sX3[s * 64 + ln] = make_uint4(pq[0].x, pq[0].y, pq[1].x, pq[1].y);
+      sX3[(S + s) * 64 + ln] = make_uint4(pk[0].x, pk[0].y, pk[1].x, pk[1].y);
+    }
     KYr[s] = as_frag(make_uint4(py[0].x, py[0].y, py[1].x, py[1].y));
     KD[s] = make_uint4(pd[0].x, pd[0].y, pd[1].x, pd[1].y);
     store_stream(rec + R::QG + ((I * S + s) * 64 + ln) * 16, make_uint4(pg[0].x, pg[0].y, pg[1].x, pg[1].y));
@@ -410,53 +416,80 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
   // C = (k Y c) (q X)^T: lane holds [j = 16J + 4g + rr][i = 16I + r], i.e. row i of
   // Aqk / Akk at columns 16J + 4g + rr -- already the P-order A fragment of the
   // inter kernel's Aqk v' product.  Block J = I uses this wave's own k*Y.
-  auto block = [&](int J, f32x4& aq, f32x4& ak) {
-    aq = f32x4{0.f, 0.f, 0.f, 0.f};
-    ak = aq;
-    if (J > I) return;
-    const int pr = 8 + I * (I - 1) / 2 + J;   // c_IJ table row (J < I)
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      bf16x8 A;
-      if (J == I) {
-        A = KYr[s];
-      } else {
-        const float4* src = reinterpret_cast<const float4*>(sKY + ((J * S + s) * 64 + ln) * 8);
-        const float4 a0 = src[0], a1 = src[1];
-        const float* c = sTab + pr * K + 32 * s;
-        const float4 c0 = *reinterpret_cast<const float4*>(c + 4 * g);
-        const float4 c1 = *reinterpret_cast<const float4*>(c + 16 + 4 * g);
-        const float b[8] = {a0.x * c0.x, a0.y * c0.y, a0.z * c0.z, a0.w * c0.w,
-                            a1.x * c1.x, a1.y * c1.y, a1.z * c1.z, a1.w * c1.w};
-        A = as_frag(pack8(b));
-      }
-      aq = mfma16x32(A, QX[s], aq);
-      ak = mfma16x32(A, KX[s], ak);
-    }
-  };
-  f32x4 vk[4];
-#pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2) {
+  // The ten nonzero 16x16 blocks (J <= I) are shared out as fragment pairs (row block
+  // Ib, columns 32 s2..): wave 0 takes (0, 0) and (3, 0), wave 1 (1, 0), wave 2 (2, 0)
+  // and (2, 1), wave 3 (3, 1) -- at most three blocks per wave instead of four for
+  // wave 3.  Row block 3's q X and k X reach wave 0 through LDS, its beta from sBeta.
+  auto job = [&](const int Ib, const int s2, f32x4* vko) {
+    const bool own = Ib == I;
+    const float bti = own ? bt : sBeta[16 * Ib + r];
     f32x4 vq[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int J = 2 * s2 + h;
-      f32x4 aq, ak;
-      block(J, aq, ak);
+      f32x4 aq = f32x4{0.f, 0.f, 0.f, 0.f}, ak = aq;
+      if (J <= Ib) {
+        const int pr = 8 + Ib * (Ib - 1) / 2 + J;   // c_IJ table row (J < Ib)
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          bf16x8 A;
+          if (J == Ib) {
+            A = KYr[s];   // only when own
+          } else {
+            const float4* src = reinterpret_cast<const float4*>(sKY + ((J * S + s) * 64 + ln) * 8);
+            const float4 a0 = src[0], a1 = src[1];
+            const float* c = sTab + pr * K + 32 * s;
+            const float4 c0 = *reinterpret_cast<const float4*>(c + 4 * g);
+            const float4 c1 = *reinterpret_cast<const float4*>(c + 16 + 4 * g);
+            const float b[8] = {a0.x * c0.x, a0.y * c0.y, a0.z * c0.z, a0.w * c0.w,
+                                a1.x * c1.x, a1.y * c1.y, a1.z * c1.z, a1.w * c1.w};
+            A = as_frag(pack8(b));
+          }
+          const bf16x8 bq = own ? QX[s] : as_frag(sX3[s * 64 + ln]);
+          const bf16x8 bk = own ? KX[s] : as_frag(sX3[(S + s) * 64 + ln]);
+          aq = mfma16x32(A, bq, aq);
+          ak = mfma16x32(A, bk, ak);
+        }
+      }
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int j = 4 * g + rr;   // column within block J
-        vq[h][rr] = (J < I || (J == I && j <= r)) ? p.scale * aq[rr] : 0.f;
-        vk[J][rr] = (J < I || (J == I && j < r)) ? -bt * ak[rr] : 0.f;   // -Akk
+        vq[h][rr] = (J < Ib || (J == Ib && j <= r)) ? p.scale * aq[rr] : 0.f;
+        vko[h][rr] = (J < Ib || (J == Ib && j < r)) ? -bti * ak[rr] : 0.f;   // -Akk
       }
     }
-    if (s2 < tri_steps(I))
-      store_stream(rec + R::AQK + (tri_frag(I, s2) * 64 + ln) * 16, pack_pair(vq[0], vq[1]));
+    store_stream(rec + R::AQK + (tri_frag(Ib, s2) * 64 + ln) * 16, pack_pair(vq[0], vq[1]));
+  };
+  f32x4 vkA[2], vkB[2];
+  if (I == 0) {
+    job(0, 0, vkA);
+    job(3, 0, vkB);
+  } else if (I == 1) {
+    job(1, 0, vkA);
+  } else if (I == 2) {
+    job(2, 0, vkA);
+    job(2, 1, vkB);
+  } else {
+    job(3, 1, vkA);
   }
   __syncthreads();  // B4: every read of k*Y is done (Akk reuses its space)
+  auto put_akk = [&](int Ib, int s2, const f32x4* v) {
 #pragma unroll
-  for (int J = 0; J < 4; ++J)
-    *reinterpret_cast<float4*>(sAkk + i * SM::AS + 16 * J + 4 * g) = make_float4(vk[J][0], vk[J][1], vk[J][2], vk[J][3]);
+    for (int h = 0; h < 2; ++h)
+      *reinterpret_cast<float4*>(sAkk + (16 * Ib + r) * SM::AS + 16 * (2 * s2 + h) + 4 * g) =
+          make_float4(v[h][0], v[h][1], v[h][2], v[h][3]);
+  };
+  if (I == 0) {
+    put_akk(0, 0, vkA);
+    put_akk(3, 0, vkB);
+  } else if (I == 1) {
+    put_akk(1, 0, vkA);
+  } else if (I == 2) {
+    put_akk(2, 0, vkA);
+    put_akk(2, 1, vkB);
+  } else {
+    put_akk(3, 1, vkA);
+  }
   __syncthreads();  // B5: Akk and (k exp(Gam))^T complete
   fetch_part(next, next_row, next_len, 0);   // q of the next item
 
