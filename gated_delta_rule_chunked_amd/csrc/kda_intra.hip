@@ -19,10 +19,12 @@
 //   block J < I:  exp(Gam_i - Gam_j) = X_i * exp(mu_I - mu_J) * Y_j
 // so Aqk/Akk run on bf16 MFMA with two exponentials per element.  Each factor is
 // bounded by exp(8 |g|) (half a block of decay), which stays finite for per-token
-// gates g >= -11 (natural log).  The Gam-referenced outputs are rebuilt from the
+// gates g >= -11 (natural log; lower gates are raised to -11 when loaded).  The
+// Gam-referenced outputs are rebuilt from the
 // same factors: exp(Gam_i) = X_i exp(mu_I), exp(Gam_last - Gam_i) = Y_i exp(Gam_last - mu_I).
 //
-// Wave I owns rows 16I..16I+15 through the gate and Aqk/Akk phases; lane
+// Wave I owns rows 16I..16I+15 through the gate phase (the Aqk/Akk blocks are then
+// shared out evenly, see phase 2); lane
 // l = 16g + r holds row 16I + r and the P-order key dims 32s + pidx(g, e)
 // (s = 0..K/32-1, e = 0..7), which is at once an MFMA A/B fragment and the qg
 // record layout.  Results leave the MFMA C layout directly as record fragments:
