@@ -90,9 +90,14 @@ int check_shapes(const kda_fwd_args* a, kda::WsLayout* L) {
   const int64_t recs = max_chunks * a->HV * L->rec_bytes;
   // header: counter | varlen: chunk table (N + 2) | segment table (N + 1, segmented scan) | chunk info
   L->cinfo_off = 0;
+  L->order_off = 0;
   int64_t head = 16;
   if (a->cu_seqlens) {
     head += ((int64_t)a->N + 2) * 4 + (seg_path ? ((int64_t)a->N + 1) * 4 : 0);
+    if (seg_path && !multi && a->N <= kda::ORDER_MAX_N) {   // one scan per sequence: longest first
+      L->order_off = head;
+      head += (int64_t)a->N * 4;
+    }
     L->cinfo_off = (head + 7) / 8 * 8;
     head = L->cinfo_off + max_chunks * 8;
   }
@@ -146,6 +151,7 @@ int check_call(const kda_fwd_args* a, int need, kda::Params* p) {
   p->table = a->cu_seqlens ? (int32_t*)(ws + 16) : nullptr;
   p->segtab = (a->cu_seqlens && L.seg_path) ? (int32_t*)(ws + 16 + ((int64_t)a->N + 2) * 4) : nullptr;
   p->cinfo = a->cu_seqlens ? (int2*)(ws + L.cinfo_off) : nullptr;
+  p->order = L.order_off ? (int32_t*)(ws + L.order_off) : nullptr;
   p->recs = ws + L.table_bytes;
   p->bbuf = L.m_off > L.b_off ? (float*)(ws + L.b_off) : nullptr;
   p->mbuf = L.total_bytes > L.m_off ? (uint16_t*)(ws + L.m_off) : nullptr;
@@ -191,7 +197,7 @@ int check_bwd_shapes(const kda_bwd_dhu_args* a, int64_t* ws_bytes) {
 int run_intra(const kda::Params& p, hipStream_t s) {
   if (p.max_chunks * p.HV == 0) return KDA_OK;
   int st = hip_status(p.cu ? kda::launch_chunk_table(p.cu, p.N, p.T, p.max_chunks, p.table, p.counter, p.seg_L,
-                                                     p.max_segs, p.segtab, p.cinfo, s)
+                                                     p.max_segs, p.segtab, p.cinfo, p.order, s)
                            : kda::launch_prep(p, s));
   if (st != KDA_OK) return st;
   return hip_status(kda::launch_intra(p, s));
@@ -299,7 +305,7 @@ int kda_bwd_dhu(const kda_bwd_dhu_args* a) {
   hipStream_t s = (hipStream_t)a->stream;
   if (a->cu_seqlens) {
     const int64_t cap = p.NT + (int64_t)p.N;   // upper bound on the chunk count
-    st = hip_status(kda::launch_chunk_table(p.cu, p.N, p.T, cap, p.table, nullptr, 1, 0, nullptr, nullptr, s));
+    st = hip_status(kda::launch_chunk_table(p.cu, p.N, p.T, cap, p.table, nullptr, 1, 0, nullptr, nullptr, nullptr, s));
     if (st != KDA_OK) return st;
   }
   return hip_status(kda::launch_bwd_dhu(p, s));

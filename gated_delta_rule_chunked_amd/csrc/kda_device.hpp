@@ -232,6 +232,8 @@ struct WsLayout {
   bool seg_path;        // the segmented scan is used
   int seg_L, seg_S;     // chunks per segment; fixed length: segments per sequence
   int64_t max_segs;
+  int64_t order_off;    // varlen, one segment per sequence: byte offset of the longest-first
+                        // sequence order (int32 [N]), or 0 when the scan keeps the given order
 };
 
 }  // namespace kda

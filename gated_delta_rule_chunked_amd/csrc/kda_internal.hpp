@@ -39,6 +39,7 @@ struct Params {
   int seg_S;             // fixed length: segments per sequence
   int64_t max_segs;      // capacity of the segment buffers (segments over all sequences)
   int32_t* segtab;       // varlen: seg_base[N+1] in the workspace header, else nullptr
+  int32_t* order;        // varlen, one segment per sequence: sequences longest first, else nullptr
   float* bbuf;           // K x V fp32 segment end states per (segment, HV), in the column
                          // waves' C-layout order (kda_scan.hip), or nullptr (one segment)
   uint16_t* mbuf;        // K x K bf16 segment transitions per (segment, HV), as P-order A
@@ -69,10 +70,12 @@ struct BwdParams {
 // varlen chunk table (chunk_base[N+1], error flag at [N+1]); also zeroes *counter when
 // non-null, writes seg_base[N+1] (segments of seg_L chunks, at least one per
 // sequence) when segtab is non-null and per-chunk {first row, valid rows} when
-// cinfo is non-null
+// cinfo is non-null, and the sequences ordered by chunk count, longest first, when
+// order is non-null (N <= ORDER_MAX_N)
 hipError_t launch_chunk_table(const int64_t* cu, int N, int T, int64_t max_chunks, int32_t* table,
                               int32_t* counter, int seg_L, int64_t max_segs, int32_t* segtab, int2* cinfo,
-                              hipStream_t s);
+                              int32_t* order, hipStream_t s);
+constexpr int ORDER_MAX_N = 2048;   // longest-first order: sorted on one workgroup up to this many sequences
 int device_cus();                                               // compute units of the current device
 hipError_t launch_prep(const Params& p, hipStream_t s);          // fixed length: zeroes the counter
 hipError_t launch_intra(const Params& p, hipStream_t s);

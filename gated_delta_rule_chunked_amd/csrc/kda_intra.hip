@@ -93,13 +93,17 @@ __device__ __forceinline__ bool locate_chunk(const Params& p, const int32_t* __r
 // FlashKDA walkthrough's sequence-information section), chunk_base[N] = total,
 // and an error flag at [N+1] if cu_seqlens is not 0 = cu[0] <= ... <= cu[N] = T;
 // optionally the segment table and, per chunk, its first row and valid rows (so the
-// intra stage finds a chunk with one load instead of a search over the table).
+// intra stage finds a chunk with one load instead of a search over the table), and
+// the sequences sorted by chunk count, longest first (ties by index), so that the
+// 64-column scan can hand out its longest scans first.
 __global__ __launch_bounds__(256) void chunk_table_kernel(const int64_t* cu, int N, int T, int64_t max_chunks,
                                                            int32_t* table, int32_t* counter, int seg_L,
-                                                           int64_t max_segs, int32_t* segtab, int2* cinfo) {
+                                                           int64_t max_segs, int32_t* segtab, int2* cinfo,
+                                                           int32_t* order) {
   __shared__ int32_t scan[256];
   __shared__ int32_t sscan[256];
   __shared__ int32_t bad_any;
+  __shared__ unsigned long long skey[ORDER_MAX_N];   // chunk count << 32 | ~index: larger key first
   const int tid = threadIdx.x;
   if (tid == 0) {
     bad_any = (cu[0] != 0 || cu[N] != T) ? 1 : 0;
@@ -118,6 +122,7 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int64_t* cu, int
     }
     scan[tid] = cnt;
     sscan[tid] = scnt;
+    if (order && n < N) skey[n] = ((unsigned long long)(uint32_t)cnt << 32) | (0xffffffffu - (uint32_t)n);
     __syncthreads();
     for (int off = 1; off < 256; off <<= 1) {
       const int32_t add = tid >= off ? scan[tid - off] : 0;
@@ -140,6 +145,28 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int64_t* cu, int
     running += scan[255];
     srunning += sscan[255];
     __syncthreads();
+  }
+  if (order) {
+    // bitonic sort of the keys, descending; padding keys are 0 and sort last
+    int P = 1;
+    while (P < N) P <<= 1;
+    for (int n = N + tid; n < P; n += 256) skey[n] = 0ull;
+    __syncthreads();
+    for (int k = 2; k <= P; k <<= 1)
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < P; i += 256) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const unsigned long long a = skey[i], b = skey[ixj];
+            if (((i & k) == 0) ? (a < b) : (a > b)) {
+              skey[i] = b;
+              skey[ixj] = a;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    for (int r = tid; r < N; r += 256) order[r] = (int32_t)(0xffffffffu - (uint32_t)(skey[r] & 0xffffffffull));
   }
   if (tid == 0) {
     table[N] = running;
@@ -687,9 +714,10 @@ static int padded8(int64_t n) { return (int)((n + 7) / 8 * 8); }
 
 hipError_t launch_chunk_table(const int64_t* cu, int N, int T, int64_t max_chunks, int32_t* table,
                               int32_t* counter, int seg_L, int64_t max_segs, int32_t* segtab, int2* cinfo,
-                              hipStream_t s) {
+                              int32_t* order, hipStream_t s) {
+  if (order && N > ORDER_MAX_N) return hipErrorInvalidValue;
   hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, s, cu, N, T, max_chunks, table, counter,
-                     seg_L, max_segs, segtab, cinfo);
+                     seg_L, max_segs, segtab, cinfo, order);
   return hipGetLastError();
 }
 

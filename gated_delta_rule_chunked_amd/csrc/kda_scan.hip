@@ -521,7 +521,10 @@ __global__ __launch_bounds__(SCAN_STATE_THREADS, 1) void scan_state_kernel(Param
 template <int K>
 __global__ __launch_bounds__(SCAN_THREADS, 1) void scan_full_kernel(Params p, int n_items) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[ScanSmem<K, SCAN_FULL>::BYTES];
-  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  // with the longest-first order every workgroup of the grid is mapped below; otherwise
+  // items are XCD-remapped and the grid's padding returns here
+  const int item = p.order ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
+  if (p.order) n_items = (int)gridDim.x;
   if (item >= n_items) return;
   const int tid = threadIdx.x;
   if (p.cu != nullptr && p.table[p.N + 1] != 0) {
@@ -537,9 +540,24 @@ __global__ __launch_bounds__(SCAN_THREADS, 1) void scan_full_kernel(Params p, in
     return;
   }
   const int NCG = (p.V + 63) / 64;
-  const int cg = item % NCG;
-  const int hv = (item / NCG) % p.HV;
-  const int64_t sigma = item / (NCG * p.HV);
+  int cg, hv;
+  int64_t sigma;
+  if (p.order) {
+    // varlen, one segment per sequence: (sequence rank, head) units in dispatch order,
+    // so the longest sequences start first; a unit's column groups go to one XCD (the
+    // unit picks the XCD, its column groups follow in consecutive rounds of eight)
+    const int b = blockIdx.x, rnd = b >> 3;
+    const int64_t u = (int64_t)(rnd / NCG) * 8 + (b & 7);
+    if (u >= (int64_t)p.N * p.HV) return;
+    cg = rnd % NCG;
+    hv = (int)(u % p.HV);
+    sigma = p.order[u / p.HV];
+    if ((uint64_t)sigma >= (uint64_t)p.N) return;   // never for an order the chunk table wrote
+  } else {
+    cg = item % NCG;
+    hv = (item / NCG) % p.HV;
+    sigma = item / (NCG * p.HV);
+  }
   SegLoc sl;
   if (!locate_segment(p, sigma, sl)) return;
   scan_body<K, SCAN_FULL>(p, smem, sl, hv, cg, min(4, (p.V - 64 * cg) / BV), sigma);
@@ -556,8 +574,9 @@ static hipError_t launch_scan_k(const Params& p, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const int64_t items = p.max_segs * p.HV * NCG;
-  hipLaunchKernelGGL((scan_full_kernel<K>), dim3((int)((items + 7) / 8 * 8)), dim3(SCAN_THREADS), 0, s, p,
-                     (int)items);
+  // longest-first order: whole rounds of eight units, NCG workgroups each
+  const int64_t grid = p.order ? ((int64_t)p.N * p.HV + 7) / 8 * 8 * NCG : (items + 7) / 8 * 8;
+  hipLaunchKernelGGL((scan_full_kernel<K>), dim3((int)grid), dim3(SCAN_THREADS), 0, s, p, (int)items);
   return hipGetLastError();
 }
 

@@ -99,9 +99,10 @@ def test_workspace_bytes(lib):
     st, n = ws(args(B=1, T=1000, HQK=1, HV=2, N=5, cu_seqlens=1 << 20))
     assert st == 0 and n == 256 + (16 + 5) * 2 * 61952
     # N=70: 70 x 2 x 2 = 280 wide workgroups fill the device: one segment per sequence;
-    # header 16 + 72 x 4 + 71 x 4 (segment table) = 588, chunk info from 592: + 86 x 8 = 1280
+    # header 16 + 72 x 4 + 71 x 4 (segment table) + 70 x 4 (longest-first order) = 868,
+    # chunk info from 872: + 86 x 8 = 1560 -> 1792
     st, n = ws(args(B=1, T=1000, HQK=1, HV=2, N=70, cu_seqlens=1 << 20))
-    assert st == 0 and n == 1280 + (16 + 70) * 2 * 61952 + 1024
+    assert st == 0 and n == 1792 + (16 + 70) * 2 * 61952 + 1024
     # T=16384, H=2: 16 serial workgroups, 256 chunks -> segmented, L = max(8, 256/8) = 32, 8 segments
     st, n = ws(args(B=1, T=16384, HQK=2, HV=2))
     assert st == 0 and n == 256 + 256 * 2 * 61952 + 1024 + 8 * 2 * (KV4 + KK2)

@@ -110,3 +110,30 @@ def test_automatic_segmented_scan_long_sequence_few_heads():
     eo, eh = nerr(o, o_ref), nerr(ht, ht_ref)
     print(f"  auto segmented: o {eo:.2e} ht {eh:.2e}", flush=True)
     assert eo <= TOL and eh <= TOL
+
+
+def test_varlen_many_sequences_longest_first_order():
+    # 70 sequences x 2 heads x 2 column groups = 280 wide workgroups fill the device, so
+    # the library runs one 64-column scan per sequence and hands them out longest first
+    # (the chunk table kernel sorts the sequences on the device).  Every o row must be
+    # written exactly by its own scan: the output starts as NaN.
+    import torch
+    from gated_delta_rule_chunked_amd import kda_fwd, kda_fwd_scan_plan, make_args
+    rng = np.random.default_rng(140)
+    lengths = [int(x) for x in rng.integers(0, 260, size=70)]
+    lengths[3], lengths[40] = 0, 1
+    d = make_inputs(141, B=1, T=0, HQK=1, HV=2, K=128, V=128, has_h0=True, lengths=lengths)
+    t = to_device(d)
+    o = torch.full(t["v"].shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    a = make_args(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], t["h0"], t["cu_seqlens"], o, None)
+    assert kda_fwd_scan_plan(a) >= max(1, -(-max(lengths) // 64))   # one segment per sequence
+    out = kda_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=d["scale"], h0=t["h0"],
+                  cu_seqlens=t["cu_seqlens"], o=o)
+    torch.cuda.synchronize()
+    o_np, ht_np = [x.float().cpu().numpy().astype(np.float64) for x in out]
+    assert np.all(np.isfinite(o_np))
+    o_ref, ht_ref = reference(d)
+    eo, eh = nerr(o_np, o_ref), nerr(ht_np, ht_ref)
+    print(f"  70 sequences: o {eo:.2e} ht {eh:.2e}", flush=True)
+    assert eo <= TOL and eh <= TOL
+    assert np.array_equal(ht_np[3], d["h0"][3].astype(np.float64))
