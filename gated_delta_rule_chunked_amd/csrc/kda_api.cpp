@@ -94,7 +94,7 @@ int check_shapes(const kda_fwd_args* a, kda::WsLayout* L) {
   int64_t head = 16;
   if (a->cu_seqlens) {
     head += ((int64_t)a->N + 2) * 4 + (seg_path ? ((int64_t)a->N + 1) * 4 : 0);
-    if (seg_path && !multi && a->N <= kda::ORDER_MAX_N) {   // one scan per sequence: longest first
+    if (!multi && a->N <= kda::ORDER_MAX_N) {   // one scan per (sequence, head, tile): longest first
       L->order_off = head;
       head += (int64_t)a->N * 4;
     }
@@ -190,7 +190,10 @@ int check_bwd_shapes(const kda_bwd_dhu_args* a, int64_t* ws_bytes) {
   if (max_chunks * a->HV >= ((int64_t)1 << 31) - 8) return KDA_ERR_INVALID_ARG;
   if ((int64_t)a->N * a->HV * (a->V / kda::BV) >= ((int64_t)1 << 31) - 8) return KDA_ERR_INVALID_ARG;
   if (a->N >= (1 << 30)) return KDA_ERR_INVALID_ARG;
-  *ws_bytes = a->cu_seqlens ? (((int64_t)a->N + 2) * 4 + 255) / 256 * 256 : 0;
+  // varlen: the chunk table (N + 2 int32) and, up to ORDER_MAX_N sequences, the
+  // longest-first sequence order (N int32)
+  const int64_t order_words = a->N <= kda::ORDER_MAX_N ? a->N : 0;
+  *ws_bytes = a->cu_seqlens ? (((int64_t)a->N + 2 + order_words) * 4 + 255) / 256 * 256 : 0;
   return KDA_OK;
 }
 
@@ -298,6 +301,7 @@ int kda_bwd_dhu(const kda_bwd_dhu_args* a) {
   p.dh0 = a->dh0;
   p.dhc = a->dhc;
   p.table = a->cu_seqlens ? (int32_t*)a->workspace : nullptr;
+  p.order = (a->cu_seqlens && a->N <= kda::ORDER_MAX_N) ? p.table + a->N + 2 : nullptr;
   p.scale = a->scale;
   p.flags = a->flags;
   p.B = a->B; p.T = a->T; p.HV = a->HV; p.K = a->K; p.V = a->V; p.N = a->N;
@@ -305,7 +309,7 @@ int kda_bwd_dhu(const kda_bwd_dhu_args* a) {
   hipStream_t s = (hipStream_t)a->stream;
   if (a->cu_seqlens) {
     const int64_t cap = p.NT + (int64_t)p.N;   // upper bound on the chunk count
-    st = hip_status(kda::launch_chunk_table(p.cu, p.N, p.T, cap, p.table, nullptr, 1, 0, nullptr, nullptr, nullptr, s));
+    st = hip_status(kda::launch_chunk_table(p.cu, p.N, p.T, cap, p.table, nullptr, 1, 0, nullptr, nullptr, p.order, s));
     if (st != KDA_OK) return st;
   }
   return hip_status(kda::launch_bwd_dhu(p, s));

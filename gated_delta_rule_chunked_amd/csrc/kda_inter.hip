@@ -75,12 +75,29 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void inter_kernel(Params p, int n
   constexpr int S = K / 32, ND = K / 16, PF = OUT_RING - 1;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SM::BYTES];
 
-  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  // With the longest-first order (varlen) every workgroup of the grid is mapped to a
+  // (sequence rank, head) unit in dispatch order, a unit's tiles following in
+  // consecutive rounds of eight on one XCD; otherwise items are XCD-remapped.
+  const bool lpt = p.order != nullptr;
+  const int item = lpt ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
+  if (lpt) n_items = (int)gridDim.x;
   if (item >= n_items) return;
   const int NVT = p.V / BV;
-  const int vt = item % NVT;
-  const int hv = (item / NVT) % p.HV;
-  const int n = item / (NVT * p.HV);
+  int vt, hv, n;
+  bool unit_ok = true;
+  if (lpt) {
+    const int rnd = item >> 3;
+    const int64_t u = (int64_t)(rnd / NVT) * 8 + (item & 7);
+    unit_ok = u < (int64_t)p.N * p.HV;
+    vt = rnd % NVT;
+    hv = unit_ok ? (int)(u % p.HV) : 0;
+    n = unit_ok ? p.order[u / p.HV] : 0;
+    if ((unsigned)n >= (unsigned)p.N) unit_ok = false, n = 0;   // never for an order the chunk table wrote
+  } else {
+    vt = item % NVT;
+    hv = (item / NVT) % p.HV;
+    n = item / (NVT * p.HV);
+  }
   const int tid = threadIdx.x, ln = tid & 63, r = ln & 15, g = ln >> 4;
   // The wave index goes through readfirstlane so that every branch on it is a
   // scalar branch: an MFMA under a lane-predicated branch still writes all lanes.
@@ -93,7 +110,7 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void inter_kernel(Params p, int n
     if (p.table[p.N + 1] != 0) {
       // rejected cu_seqlens: poison this tile's ht and, grid-strided, all of o
       const float qnan = __builtin_nanf("");
-      if (p.ht)
+      if (p.ht && unit_ok)
         for (int idx = tid; idx < K * BV; idx += INTER_THREADS)
           store_state(p.flags & FLAG_STATE_BF16, p.ht, (((int64_t)n * p.HV + hv) * K + idx / BV) * p.V + vt * BV + idx % BV, qnan);
       const int64_t total = (int64_t)p.B * p.T * p.HV * p.V;
@@ -101,6 +118,7 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void inter_kernel(Params p, int n
         p.o[idx] = 0x7fc0;
       return;
     }
+    if (!unit_ok) return;
     sq.b = 0; sq.bos = p.cu[n]; sq.len = (int)(p.cu[n + 1] - p.cu[n]); sq.cbase = p.table[n];
   }
   const int nc = (sq.len + BT - 1) / BT;
@@ -344,7 +362,8 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void inter_kernel(Params p, int n
 hipError_t launch_inter(const Params& p, hipStream_t s) {
   const int64_t items = (int64_t)p.N * p.HV * (p.V / BV);
   if (items == 0) return hipSuccess;
-  const int grid = (int)((items + 7) / 8 * 8);
+  // longest-first order: whole rounds of eight units, V / 16 workgroups each
+  const int grid = (int)(p.order ? ((int64_t)p.N * p.HV + 7) / 8 * 8 * (p.V / BV) : (items + 7) / 8 * 8);
   if (p.K == 128)
     hipLaunchKernelGGL((inter_kernel<128>), dim3(grid), dim3(INTER_THREADS), 0, s, p, (int)items);
   else

@@ -60,6 +60,7 @@ struct BwdParams {
   void* dh0;             // state dtype, or nullptr
   void* dhc;             // checkpoint dtype, or nullptr
   int32_t* table;        // varlen chunk table (workspace) or nullptr
+  int32_t* order;        // varlen: sequences longest first (workspace), or nullptr
   float scale;
   uint32_t flags;        // FLAG_STATE_BF16, FLAG_CKPT_BF16
   int B, T, HV, K, V, N;

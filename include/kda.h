@@ -208,7 +208,8 @@ typedef struct kda_bwd_dhu_args {
   void* dh0;
   void* dhc;
   /* Scratch (device, 256-byte aligned, size from kda_bwd_dhu_workspace_bytes;
-   * zero bytes, so NULL is allowed, for fixed length). */
+   * zero bytes, so NULL is allowed, for fixed length; varlen: the chunk table and
+   * the sequences' longest-first order, written by the call itself). */
   void* workspace;
   size_t workspace_bytes;
   void* stream;                /* hipStream_t */

@@ -208,10 +208,12 @@ def bwd_ws(a):
 
 
 def test_bwd_workspace_bytes(lib):
-    # fixed length needs no scratch; varlen holds the chunk table (N + 2 int32)
+    # fixed length needs no scratch; varlen holds the chunk table (N + 2 int32) and the
+    # longest-first sequence order (N int32, up to 2048 sequences)
     assert bwd_ws(bwd_args(B=1, T=8192, HV=32)) == (0, 0)
     assert bwd_ws(bwd_args(N=5, cu_seqlens=1 << 20)) == (0, 256)
-    assert bwd_ws(bwd_args(N=70, cu_seqlens=1 << 20)) == (0, 512)
+    assert bwd_ws(bwd_args(N=70, cu_seqlens=1 << 20)) == (0, 768)
+    assert bwd_ws(bwd_args(N=3000, cu_seqlens=1 << 20)) == (0, (3002 * 4 + 255) // 256 * 256)
     assert bwd_ws(bwd_args(K=96))[0] == K.KDA_ERR_UNSUPPORTED
     assert lib.kda_bwd_dhu_workspace_bytes(None, None) == K.KDA_ERR_INVALID_ARG
 

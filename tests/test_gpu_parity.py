@@ -260,3 +260,26 @@ def test_rejected_cu_seqlens_poisons_outputs():
     d["cu_seqlens"] = np.array([0, 100, 50, 200], dtype=np.int64)   # not non-decreasing
     o, ht = run_hip(d)
     assert np.all(np.isnan(o)) and np.all(np.isnan(ht))
+
+
+def test_varlen_serial_scan_longest_first_order():
+    # 40 short sequences x 3 heads: the 16-column serial scan, its (sequence, head)
+    # units handed out longest first (120 units, not a multiple of the eight XCDs);
+    # every o row is checked, starting from NaN
+    import torch
+    from gated_delta_rule_chunked_amd import kda_fwd, kda_fwd_scan_plan, make_args
+    rng = np.random.default_rng(146)
+    lengths = [int(x) for x in rng.integers(0, 200, size=40)]
+    lengths[7] = 0
+    d = make_inputs(147, B=1, T=0, HQK=3, HV=3, K=128, V=128, has_h0=True, lengths=lengths)
+    t = to_device(d)
+    o = torch.full(t["v"].shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    a = make_args(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], t["h0"], t["cu_seqlens"], o, None)
+    assert kda_fwd_scan_plan(a) == 0   # the serial scan
+    out = kda_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=d["scale"], h0=t["h0"],
+                  cu_seqlens=t["cu_seqlens"], o=o)
+    torch.cuda.synchronize()
+    o_np, ht_np = [x.float().cpu().numpy().astype(np.float64) for x in out]
+    assert np.all(np.isfinite(o_np))
+    check(o_np, ht_np, *full_oracle(d))
+    assert np.array_equal(ht_np[7], d["h0"][7].astype(np.float64))
