@@ -146,7 +146,16 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int64_t* cu, int
     srunning += sscan[255];
     __syncthreads();
   }
-  if (order) {
+  if (order && N <= 256) {
+    // rank of each key among the N distinct keys (one pass over LDS, no sort rounds)
+    __syncthreads();
+    if (tid < N) {
+      const unsigned long long key = skey[tid];
+      int rank = 0;
+      for (int m = 0; m < N; ++m) rank += skey[m] > key;
+      order[rank] = tid;
+    }
+  } else if (order) {
     // bitonic sort of the keys, descending; padding keys are 0 and sort last
     int P = 1;
     while (P < N) P <<= 1;

@@ -137,3 +137,27 @@ def test_varlen_many_sequences_longest_first_order():
     print(f"  70 sequences: o {eo:.2e} ht {eh:.2e}", flush=True)
     assert eo <= TOL and eh <= TOL
     assert np.array_equal(ht_np[3], d["h0"][3].astype(np.float64))
+
+
+def test_varlen_300_sequences_sorted_on_the_device():
+    # 300 sequences (more than one workgroup's worth, so the chunk table kernel sorts
+    # them with its bitonic network rather than by rank) through the 64-column scan,
+    # one per sequence, longest first; every o row checked, starting from NaN
+    import torch
+    from gated_delta_rule_chunked_amd import kda_fwd
+    rng = np.random.default_rng(148)
+    lengths = [int(x) for x in rng.integers(0, 150, size=300)]
+    lengths[10] = 0
+    d = make_inputs(149, B=1, T=0, HQK=1, HV=1, K=64, V=64, has_h0=True, lengths=lengths)
+    t = to_device(d)
+    o = torch.full(t["v"].shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = kda_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=d["scale"], h0=t["h0"],
+                  cu_seqlens=t["cu_seqlens"], o=o)
+    torch.cuda.synchronize()
+    o_np, ht_np = [x.float().cpu().numpy().astype(np.float64) for x in out]
+    assert np.all(np.isfinite(o_np))
+    o_ref, ht_ref = reference(d)
+    eo, eh = nerr(o_np, o_ref), nerr(ht_np, ht_ref)
+    print(f"  300 sequences: o {eo:.2e} ht {eh:.2e}", flush=True)
+    assert eo <= TOL and eh <= TOL
+    assert np.array_equal(ht_np[10], d["h0"][10].astype(np.float64))
