@@ -133,6 +133,8 @@ def test_scan_plan(lib):
     assert plan(B=1, T=16384, HQK=2, HV=2) == 32                 # 8 segments
     assert plan(B=1, T=8192, HQK=32, HV=32, seg_chunks=5) == 5   # forced
     assert plan(B=1, T=200, HQK=1, HV=1) == 0
+    assert plan(B=2, T=2048, HQK=4, HV=4, N=2) == 4              # 32 chunks, 64 serial workgroups: 8 segments
+    assert plan(B=2, T=1984, HQK=4, HV=4, N=2) == 0              # 31 chunks: serial
     n = ctypes.c_int32(0)
     assert lib.kda_fwd_scan_plan(None, ctypes.byref(n)) == K.KDA_ERR_INVALID_ARG
     assert lib.kda_fwd_scan_plan(ctypes.byref(args()), None) == K.KDA_ERR_INVALID_ARG
