@@ -161,3 +161,25 @@ def test_varlen_300_sequences_sorted_on_the_device():
     print(f"  300 sequences: o {eo:.2e} ht {eh:.2e}", flush=True)
     assert eo <= TOL and eh <= TOL
     assert np.array_equal(ht_np[10], d["h0"][10].astype(np.float64))
+
+
+@pytest.mark.parametrize("n_seq", [2048, 2049])
+def test_varlen_order_limit(n_seq):
+    # at the limit of the device sort (2048 sequences, bitonic network over the whole
+    # LDS key array) and one past it (the given order); sequences of 0 to 3 tokens
+    import torch
+    from gated_delta_rule_chunked_amd import kda_fwd
+    rng = np.random.default_rng(150 + n_seq)
+    lengths = [int(x) for x in rng.integers(0, 4, size=n_seq)]
+    d = make_inputs(151, B=1, T=0, HQK=1, HV=1, K=64, V=64, has_h0=True, lengths=lengths)
+    t = to_device(d)
+    o = torch.full(t["v"].shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = kda_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=d["scale"], h0=t["h0"],
+                  cu_seqlens=t["cu_seqlens"], o=o)
+    torch.cuda.synchronize()
+    o_np, ht_np = [x.float().cpu().numpy().astype(np.float64) for x in out]
+    assert np.all(np.isfinite(o_np))
+    o_ref, ht_ref = reference(d)
+    eo, eh = nerr(o_np, o_ref), nerr(ht_np, ht_ref)
+    print(f"  {n_seq} sequences: o {eo:.2e} ht {eh:.2e}", flush=True)
+    assert eo <= TOL and eh <= TOL
