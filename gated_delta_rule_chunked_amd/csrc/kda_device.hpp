@@ -204,10 +204,13 @@ struct Rec {
   static constexpr int BYTES = AQK + 6 * 1024;     // 61952 (K=128), 37120 (K=64)
   static_assert(BYTES % 256 == 0 && STATE_BYTES % 256 == 0, "records stay 256-byte aligned");
 };
-// Records are stored head-major: all chunks of value head hv are contiguous, so
-// the serial scan of one head streams through consecutive memory.
-__device__ __host__ __forceinline__ int64_t rec_index(int hv, int64_t chunk, int64_t max_chunks) {
-  return (int64_t)hv * max_chunks + chunk;
+// Records are stored chunk-major: the HV records of one chunk are contiguous.
+// The scans run consecutive heads side by side at the same chunk position, so
+// the records in flight at one time sit next to each other instead of being
+// max_chunks records apart, which spreads the streams over the memory
+// channels more evenly than head-major storage did.
+__device__ __host__ __forceinline__ int64_t rec_index(int hv, int64_t chunk, int64_t nheads) {
+  return chunk * nheads + hv;
 }
 __device__ __host__ __forceinline__ constexpr int tri_frag(int mb, int s) {
   return mb < 2 ? mb : 2 * mb - 2 + s;   // (0,0)0 (1,0)1 (2,0)2 (2,1)3 (3,0)4 (3,1)5

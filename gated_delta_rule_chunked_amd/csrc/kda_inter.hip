@@ -65,7 +65,7 @@ struct OutOps {                            // output-wave operands of one phase
 
 template <int K>
 __device__ __forceinline__ const uint8_t* rec_ptr(const Params& p, const SeqLoc& sq, int hv, int c) {
-  return p.recs + rec_index(hv, sq.cbase + c, p.max_chunks) * (int64_t)Rec<K>::BYTES;
+  return p.recs + rec_index(hv, sq.cbase + c, p.HV) * (int64_t)Rec<K>::BYTES;
 }
 
 template <int K>

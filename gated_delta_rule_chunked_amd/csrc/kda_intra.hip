@@ -334,7 +334,7 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
     cur_len = next_len;
     continue;
   }
-  uint8_t* rec = p.recs + rec_index(hv, gc, p.max_chunks) * (int64_t)R::BYTES;
+  uint8_t* rec = p.recs + rec_index(hv, gc, p.HV) * (int64_t)R::BYTES;
   if (g == 0) sBeta[i] = bt;
 
   // in-block inclusive cumsum over the 16 rows (lanes r = 0..15 of a DPP row)
@@ -670,7 +670,7 @@ __global__ __launch_bounds__(NTHREADS) void unpack_kernel(Params p, int n_items,
   const int64_t gc = item / p.HV;
   ChunkLoc cl;
   if (!locate_chunk(p, p.table, p.cinfo, gc, cl)) return;
-  const uint8_t* rec = p.recs + rec_index(hv, gc, p.max_chunks) * (int64_t)R::BYTES;
+  const uint8_t* rec = p.recs + rec_index(hv, gc, p.HV) * (int64_t)R::BYTES;
   const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, r = ln & 15, g = ln >> 4;
   auto tokrow = [&](int t) { return ((int64_t)cl.b * p.T + cl.row0 + t) * p.HV + hv; };
   const int t = 16 * wv + r;

@@ -161,7 +161,7 @@ __device__ __forceinline__ void scan_body(const Params& p, uint8_t* smem, const 
     const int vcol = min(grp * 64 + BV * vcw, p.V - BV) + 8 * vhalf;
     auto fetch = [&](int ph, u32x4* dst, uint4& v0, uint4& v1) {
       const int c = chunk_of(ph);
-      const uint8_t* rec = p.recs + rec_index(hv, sl.cbase + c, p.max_chunks) * (int64_t)R::BYTES + ln * 16;
+      const uint8_t* rec = p.recs + rec_index(hv, sl.cbase + c, p.HV) * (int64_t)R::BYTES + ln * 16;
 #pragma unroll
       for (int i = 0; i < NLD; ++i) dst[i] = *reinterpret_cast<const u32x4*>(rec + min(4 * i + lw, SM::NREG - 1) * 1024);
       if (MODE != SCAN_M) {
@@ -188,7 +188,7 @@ __device__ __forceinline__ void scan_body(const Params& p, uint8_t* smem, const 
     auto dma = [&](int ph) {
       if (SM::NLDD == 0) return;
       const int c = chunk_of(ph);
-      const uint8_t* rec = p.recs + rec_index(hv, sl.cbase + c, p.max_chunks) * (int64_t)R::BYTES + ln * 16;
+      const uint8_t* rec = p.recs + rec_index(hv, sl.cbase + c, p.HV) * (int64_t)R::BYTES + ln * 16;
       uint8_t* slot = smem + (ph & 1) * SM::SLOT;
 #pragma unroll
       for (int i = 0; i < SM::NLDD; ++i) {
