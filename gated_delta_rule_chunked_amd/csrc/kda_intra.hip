@@ -14,14 +14,19 @@
 //
 // Gate factoring.  exp(Gam_i - Gam_j) inside the d-sum cannot be pulled out, so
 // each 16-row block I gets a per-dimension reference mu_I (its cumsum midpoint)
-// and the factors X_i = exp(Gam_i - mu_I), Y_j = exp(mu_I - Gam_j):
-//   same block:   exp(Gam_i - Gam_j) = X_i Y_j
-//   block J < I:  exp(Gam_i - Gam_j) = X_i * exp(mu_I - mu_J) * Y_j
-// so Aqk/Akk run on bf16 MFMA with two exponentials per element.  Each factor is
-// bounded by exp(8 |g|) (half a block of decay), which stays finite for per-token
-// gates g >= -11 (natural log; lower gates are raised to -11 when loaded).  The
-// Gam-referenced outputs are rebuilt from the
-// same factors: exp(Gam_i) = X_i exp(mu_I), exp(Gam_last - Gam_i) = Y_i exp(Gam_last - mu_I).
+// and the factors X_i = exp(Gam_i - mu_I), Y_j = exp(mu_I - Gam_j), which give
+// the same-block products exp(Gam_i - Gam_j) = X_i Y_j.  A pair of blocks J < I
+// meets at P_{J+1}, the cumsum at the end of block J:
+//   exp(Gam_i - Gam_j) = X_i * [Y_j exp(tot_J / 2)] * exp(mu_I - P_{J+1}),
+// where the bracket equals exp(P_{J+1} - Gam_j) <= 1 and the last factor is <= 1
+// as well.  So Aqk/Akk run on bf16 MFMA with two exponentials per element, and a
+// cross-block factor that underflows only where the whole product is negligible
+// (below exp(-12) once the X_i it meets is counted).  X and Y are bounded by
+// exp(8 |g|) (half a block of decay); per-token gates below -10 (natural log) are
+// raised to -10 when loaded, which keeps both within exp(+-80), normal in fp32 and
+// bf16.  The Gam-referenced outputs are rebuilt from the same factors:
+// exp(Gam_i) = X_i exp(mu_I), exp(Gam_last - Gam_i) = Y_i exp(Gam_last - mu_I); where
+// one of those second factors underflows the product is below exp(-12) as well.
 //
 // Wave I owns rows 16I..16I+15 through the gate phase (the Aqk/Akk blocks are then
 // shared out evenly, see phase 2); lane
@@ -37,6 +42,7 @@
 #include "kda_internal.hpp"
 
 #include <algorithm>
+#include <atomic>
 
 namespace kda {
 
@@ -45,9 +51,10 @@ struct IntraSmem {
   static constexpr int S = K / 32;
   static constexpr int RS = K + 16;                     // row-major [64][K] tile row stride (bf16)
   static constexpr int TOT = 0;                         // float [4][K] block gate totals
-  static constexpr int TAB = TOT + 4 * K * 4;           // float [14][K] E, F, c tables
-  static constexpr int BETA = TAB + 14 * K * 4;         // float [64]
-  static constexpr int KY = BETA + 256;                 // float [3][S][64][8] k*Y, blocks 0..2
+  static constexpr int NTAB = 17;                       // gate table rows
+  static constexpr int TAB = TOT + 4 * K * 4;           // float [NTAB][K] E, F, c, H tables
+  static constexpr int BETA = TAB + NTAB * K * 4;       // float [64]
+  static constexpr int KY = BETA + 256;                 // float [3][S][64][8] k Y H, blocks 0..2
   static constexpr int KY_BYTES = 3 * S * 64 * 8 * 4;
   static constexpr int KT = KY + KY_BYTES;              // bf16 [64][RS]: kg
   static constexpr int KDT = KT + 64 * RS * 2;          // bf16 [64][RS]: k exp(Gam)
@@ -191,15 +198,16 @@ __global__ void prep_kernel(Params p) {
 }
 
 // ------------------------------------------------------------ intra kernel
-// Lowest per-token gate (natural log), -11, that the gate factoring takes: the factors of a
-// 16-row block are bounded by exp(8 |g|) = exp(88), finite in fp32 and bf16.  Lower
-// gates are raised to it.  That changes the decay of such a token from exp(g) to
-// exp(-11) ~ 1.7e-5, i.e. by at most 1.7e-5 of the state it multiplies, well below
-// the bf16 resolution of the outputs.  The floor is applied to the packed bf16 bits:
-// a negative bf16 value of larger magnitude has a larger unsigned 16-bit pattern,
-// positive values lie below 0x8000, so one unsigned 16-bit min per pair does it
-// (-inf, 0xff80, becomes -11; so does a NaN with its sign bit set).
-constexpr uint16_t GATE_MIN_BF16 = 0xc130;   // -11.0
+// Lowest per-token gate (natural log), -10, that the gate factoring takes: the factors of a
+// 16-row block are bounded by exp(8 |g|) = exp(80), normal in fp32 and bf16 (whose
+// smallest normal number is about exp(-87.3)).  Lower gates are raised to it.  That
+// changes the decay of such a token from exp(g) to exp(-10) ~ 4.5e-5, i.e. by at most
+// 4.5e-5 of the state it multiplies, well below the bf16 resolution of the outputs.
+// The floor is applied to the packed bf16 bits: a negative bf16 value of larger
+// magnitude has a larger unsigned 16-bit pattern, positive values lie below 0x8000, so
+// one unsigned 16-bit min per pair does it (-inf, 0xff80, becomes -10; so does a NaN
+// with its sign bit set).
+constexpr uint16_t GATE_MIN_BF16 = 0xc120;   // -10.0
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t gate_floor2(uint32_t w) {
   const u16x2 lim = {GATE_MIN_BF16, GATE_MIN_BF16};
@@ -351,19 +359,23 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
   __syncthreads();  // B1: block totals
 
   // tables, per key dim d (natural-log sums, exp2 of log2e-scaled arguments):
-  //   rows 0..3  E_I = exp(mu_I)            mu_I = prefix_I + tot_I / 2
-  //   rows 4..7  F_I = exp(Gam_last - mu_I)
-  //   rows 8..13 c_IJ = exp(mu_I - mu_J), pair (I,J) -> 8 + I(I-1)/2 + J
+  //   rows 0..3   E_I = exp(mu_I)              mu_I = P_I + tot_I / 2, P_I = sum_{J<I} tot_J
+  //   rows 4..7   F_I = exp(Gam_last - mu_I)
+  //   rows 8..13  c_IJ = exp(mu_I - P_{J+1}), pair (I,J) -> 8 + I(I-1)/2 + J
+  //   rows 14..16 H_J = exp(tot_J / 2), so that Y_j H_J = exp(P_{J+1} - Gam_j)
+  // every argument is <= 0 except the midpoint offsets folded into X and Y
   {
     constexpr int STEP = NTHREADS / K;            // table rows per pass (2 or 4)
     const int d = tid % K, r0 = tid / K;          // r0 is uniform over a wave (64 divides K)
     const float t0 = sTot[d], t1 = sTot[K + d], t2 = sTot[2 * K + d], t3 = sTot[3 * K + d];
     const float m0 = 0.5f * t0, m1 = t0 + 0.5f * t1, m2 = t0 + t1 + 0.5f * t2, m3 = t0 + t1 + t2 + 0.5f * t3;
+    const float P1 = t0, P2 = t0 + t1, P3 = t0 + t1 + t2;
     const float G = t0 + t1 + t2 + t3;
-    const float arg[14] = {m0, m1, m2, m3, G - m0, G - m1, G - m2, G - m3,
-                           m1 - m0, m2 - m0, m2 - m1, m3 - m0, m3 - m1, m3 - m2};
+    const float arg[SM::NTAB] = {m0, m1, m2, m3, G - m0, G - m1, G - m2, G - m3,
+                                 m1 - P1, m2 - P1, m2 - P2, m3 - P1, m3 - P2, m3 - P3,
+                                 0.5f * t0, 0.5f * t1, 0.5f * t2};
 #pragma unroll
-    for (int row = 0; row < 14; ++row)
+    for (int row = 0; row < SM::NTAB; ++row)
       if (row % STEP == r0) sTab[row * K + d] = __builtin_amdgcn_exp2f(LOG2E * arg[row]);
     if (r0 == 0) reinterpret_cast<float*>(rec + R::ALPHA)[d] = __builtin_amdgcn_exp2f(LOG2E * G);
   }
@@ -422,8 +434,11 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
       pd[hf] = make_uint2(pack2(kd[0], kd[1]), pack2(kd[2], kd[3]));
       *reinterpret_cast<uint2*>(kt_row + (32 * s + 16 * hf) * 2) =
           make_uint2(pack2(kgv[0], kgv[1]), pack2(kgv[2], kgv[3]));   // kg, row-major
-      if (I < 3)
-        reinterpret_cast<float4*>(sKY + ((I * S + s) * 64 + ln) * 8)[hf] = make_float4(ky[0], ky[1], ky[2], ky[3]);
+      if (I < 3) {   // k exp(P_{I+1} - Gam), the cross-block operand of the later row blocks
+        const float4 H4 = *reinterpret_cast<const float4*>(sTab + (14 + I) * K + d0);
+        reinterpret_cast<float4*>(sKY + ((I * S + s) * 64 + ln) * 8)[hf] =
+            make_float4(ky[0] * H4.x, ky[1] * H4.y, ky[2] * H4.z, ky[3] * H4.w);
+      }
     }
     QX[s] = as_frag(make_uint4(pq[0].x, pq[0].y, pq[1].x, pq[1].y));
     KX[s] = as_frag(make_uint4(pk[0].x, pk[0].y, pk[1].x, pk[1].y));
@@ -451,9 +466,9 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
     *reinterpret_cast<uint2*>(kt_row + (SM::KDT - SM::KT) + (32 * s) * 2) = make_uint2(KD[s].x, KD[s].y);
     *reinterpret_cast<uint2*>(kt_row + (SM::KDT - SM::KT) + (32 * s + 16) * 2) = make_uint2(KD[s].z, KD[s].w);
   }
-  // C = (k Y c) (q X)^T: lane holds [j = 16J + 4g + rr][i = 16I + r], i.e. row i of
+  // C = (k Y H c) (q X)^T: lane holds [j = 16J + 4g + rr][i = 16I + r], i.e. row i of
   // Aqk / Akk at columns 16J + 4g + rr -- already the P-order A fragment of the
-  // inter kernel's Aqk v' product.  Block J = I uses this wave's own k*Y.
+  // inter kernel's Aqk v' product.  Block J = I uses this wave's own k Y (no H, c).
   // The ten nonzero 16x16 blocks (J <= I) are shared out as fragment pairs (row block
   // Ib, columns 32 s2..): wave 0 takes (0, 0) and (3, 0), wave 1 (1, 0), wave 2 (2, 0)
   // and (2, 1), wave 3 (3, 1) -- at most three blocks per wave instead of four for
@@ -730,17 +745,19 @@ hipError_t launch_chunk_table(const int64_t* cu, int N, int T, int64_t max_chunk
   return hipGetLastError();
 }
 
-// Compute units of the current device (cached per device id).
+// Compute units of the current device, cached per device id.  The cache entries are
+// atomics (relaxed): threads that call the library at once may each query the count,
+// and every one stores the same value.
 int device_cus() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 hipError_t launch_prep(const Params& p, hipStream_t s) {

@@ -102,32 +102,69 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _check_tensor(name, t, shape, dtype, device, min_rows=False):
+    """Exact shape (or, with ``min_rows``, at least shape[0] rows), dtype, contiguity
+    and device of one argument tensor."""
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    ok = tuple(t.shape[1:]) == tuple(shape[1:]) and t.dim() == len(shape) and \
+        (t.shape[0] >= shape[0] if min_rows else t.shape[0] == shape[0])
+    if not ok:
+        want = ("[>=%d, " % shape[0] + ", ".join(map(str, shape[1:])) + "]") if min_rows else list(shape)
+        raise ValueError(f"{name} must have shape {want}, got {list(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other tensors on {device}")
+
+
+def max_chunks(T, N, B=1, varlen=False):
+    """Room for the chunks of every sequence: B * ceil(T/64) for fixed length; for
+    varlen (N packed sequences in T tokens) ceil(T/64) + N, an upper bound of
+    sum_n ceil(len_n / 64) that needs no look at the lengths."""
+    nt = (T + KDA_CHUNK - 1) // KDA_CHUNK
+    return nt + N if varlen else B * nt
+
+
 def make_args(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, o=None, ht=None,
               workspace=None, stream=None, flags=0, hc=None, seg_chunks=0) -> KdaFwdArgs:
     """Fill ``kda_fwd_args`` from torch tensors (shapes as in the header).
 
     q, k: [B, T, HQK, K] bf16; v: [B, T, HV, V] bf16; g: [B, T, HV, K] bf16;
     beta: [B, T, HV] bf16; h0: [N, HV, K, V] or None; cu_seqlens: int64 [N+1]
-    on the device or None; hc: [C, HV, K, V] or None.  States (h0, ht, hc) are
-    fp32, or bf16 with KDA_FLAG_STATE_BF16 in ``flags``.  Only pointers and sizes
-    are read here.
+    on the device or None; o: [B, T, HV, V] bf16; ht: [N, HV, K, V] or None;
+    hc: [C, HV, K, V] or None, C = B * ceil(T/64) for fixed length and at least
+    ceil(T/64) + N for varlen (see ``max_chunks``).  States (h0, ht, hc) are fp32,
+    or bf16 with KDA_FLAG_STATE_BF16 in ``flags``.  Every tensor must be contiguous
+    and on q's device (the C ABI sees only pointers, so this is the only check of
+    the sizes it will read and write); violations raise ValueError or TypeError.
     """
     import torch
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q and v must be 4-dimensional: [B, T, HQK, K] and [B, T, HV, V]")
     B, T, HQK, K = q.shape
     HV, V = v.shape[2], v.shape[3]
+    dev = q.device
+    if cu_seqlens is not None and (cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2):
+        raise ValueError("cu_seqlens must be a 1-dimensional int64 tensor of N + 1 >= 2 offsets")
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
     sdt = torch.bfloat16 if flags & KDA_FLAG_STATE_BF16 else torch.float32
-    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16), ("v", v, torch.bfloat16),
-                        ("g", g, torch.bfloat16), ("beta", beta, torch.bfloat16),
-                        ("h0", h0, sdt), ("cu_seqlens", cu_seqlens, torch.int64),
-                        ("o", o, torch.bfloat16), ("ht", ht, sdt), ("hc", hc, sdt)):
-        if t is not None:
-            if t.dtype != dt:
-                raise TypeError(f"{name} must be {dt}, got {t.dtype}")
-            if not t.is_contiguous():
-                raise ValueError(f"{name} must be contiguous")
+    bf = torch.bfloat16
+    C = max_chunks(T, N, B, cu_seqlens is not None)
+    for name, t, shape, dt in (("q", q, (B, T, HQK, K), bf), ("k", k, (B, T, HQK, K), bf),
+                               ("v", v, (B, T, HV, V), bf), ("g", g, (B, T, HV, K), bf),
+                               ("beta", beta, (B, T, HV), bf), ("h0", h0, (N, HV, K, V), sdt),
+                               ("cu_seqlens", cu_seqlens, (N + 1,), torch.int64),
+                               ("o", o, (B, T, HV, V), bf), ("ht", ht, (N, HV, K, V), sdt)):
+        _check_tensor(name, t, shape, dt, dev)
+    # varlen: the exact chunk count depends on the lengths, which stay on the device
+    _check_tensor("hc", hc, (C, HV, K, V), sdt, dev, min_rows=cu_seqlens is not None)
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be on a HIP device, they are on {dev}")
     if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
+        stream = torch.cuda.current_stream(dev).cuda_stream
     a = KdaFwdArgs()
     a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
     a.scale = float(K ** -0.5 if scale is None else scale)
@@ -186,8 +223,10 @@ def alloc_workspace(args: KdaFwdArgs, device):
 
 
 def num_chunks(T, cu_seqlens=None, B=1):
-    """Chunks over all sequences: B * ceil(T/64), or sum_n ceil(len_n/64) for varlen
-    (cu_seqlens is read on the host; a device tensor is copied)."""
+    """Chunks over all sequences: B * ceil(T/64), or sum_n ceil(len_n/64) for varlen.
+    For varlen this reads cu_seqlens on the host: a device tensor is copied, which
+    synchronises with the device (the forward and backward calls never do this; they
+    size per-chunk outputs by ``max_chunks``)."""
     if cu_seqlens is None:
         return B * ((T + KDA_CHUNK - 1) // KDA_CHUNK)
     cu = [int(x) for x in cu_seqlens.detach().cpu().tolist()]
@@ -196,11 +235,14 @@ def num_chunks(T, cu_seqlens=None, B=1):
 
 def kda_fwd(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, output_final_state=True,
             o=None, workspace=None, beta_logits=False, state_dtype=None, output_chunk_states=False,
-            seg_chunks=0):
+            seg_chunks=0, ht=None, hc=None):
     """Chunked KDA forward on the current stream.
 
     Returns (o, ht or None), or (o, ht or None, hc) with ``output_chunk_states``:
-    hc [C, HV, K, V] is the state before each chunk (see ``num_chunks``).
+    hc [C, HV, K, V] is the state before each chunk, chunks numbered sequence by
+    sequence.  For fixed length C = B * ceil(T/64); for varlen hc is allocated with
+    ``max_chunks`` = ceil(T/64) + N rows, of which the first sum_n ceil(len_n/64) are
+    written (the lengths are not read on the host, so the call never synchronises).
     ``beta_logits``: beta holds logits and the kernel applies the sigmoid.
     ``state_dtype``: torch.float32 (default) or torch.bfloat16 for h0, ht and hc.
     ``seg_chunks``: segment length of the state scan in chunks (0: chosen by the library).
@@ -219,10 +261,14 @@ def kda_fwd(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, output_final
     flags = (KDA_FLAG_BETA_LOGITS if beta_logits else 0) | (KDA_FLAG_STATE_BF16 if sdt == torch.bfloat16 else 0)
     if o is None:
         o = torch.empty((B, T, HV, V), dtype=torch.bfloat16, device=q.device)
-    ht = torch.empty((N, HV, K, V), dtype=sdt, device=q.device) if output_final_state else None
-    hc = None
-    if output_chunk_states:
-        hc = torch.empty((num_chunks(T, cu_seqlens, B), HV, K, V), dtype=sdt, device=q.device)
+    if ht is None and output_final_state:
+        ht = torch.empty((N, HV, K, V), dtype=sdt, device=q.device)
+    if not output_final_state:
+        ht = None
+    if output_chunk_states and hc is None:
+        hc = torch.empty((max_chunks(T, N, B, cu_seqlens is not None), HV, K, V), dtype=sdt, device=q.device)
+    if not output_chunk_states:
+        hc = None
     args = make_args(q, k, v, g, beta, scale, h0, cu_seqlens, o, ht, flags=flags, hc=hc, seg_chunks=seg_chunks)
     if workspace is None:
         workspace = alloc_workspace(args, q.device)
@@ -245,23 +291,31 @@ def make_bwd_args(qg, kg, w, g2, do, dv=None, dht=None, scale=None, cu_seqlens=N
 
     qg, kg, w: [B, T, HV, K] bf16; g2: [B, T, HV, K] fp32; do, dv, dv2: [B, T, HV, V]
     bf16; dht, dh0: [N, HV, K, V] fp32 (bf16 with KDA_FLAG_STATE_BF16); dhc:
-    [C, HV, K, V] fp32 (bf16 with KDA_FLAG_CKPT_BF16).  Only pointers and sizes are read.
+    [C, HV, K, V] fp32 (bf16 with KDA_FLAG_CKPT_BF16), C as hc of ``make_args``.
+    Shapes, dtypes, contiguity and the device are checked as in ``make_args``.
     """
     import torch
+    if qg.dim() != 4 or do.dim() != 4:
+        raise ValueError("qg and do must be 4-dimensional: [B, T, HV, K] and [B, T, HV, V]")
     B, T, HV, K = qg.shape
     V = do.shape[3]
+    dev = qg.device
+    if cu_seqlens is not None and (cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2):
+        raise ValueError("cu_seqlens must be a 1-dimensional int64 tensor of N + 1 >= 2 offsets")
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
     sdt = torch.bfloat16 if flags & KDA_FLAG_STATE_BF16 else torch.float32
     cdt = torch.bfloat16 if flags & KDA_FLAG_CKPT_BF16 else torch.float32
     bf = torch.bfloat16
-    for name, t, dt in (("qg", qg, bf), ("kg", kg, bf), ("w", w, bf), ("g2", g2, torch.float32),
-                        ("do", do, bf), ("dv", dv, bf), ("dht", dht, sdt), ("cu_seqlens", cu_seqlens, torch.int64),
-                        ("dv2", dv2, bf), ("dh0", dh0, sdt), ("dhc", dhc, cdt)):
-        if t is not None:
-            if t.dtype != dt:
-                raise TypeError(f"{name} must be {dt}, got {t.dtype}")
-            if not t.is_contiguous():
-                raise ValueError(f"{name} must be contiguous")
+    C = max_chunks(T, N, B, cu_seqlens is not None)
+    for name, t, shape, dt in (("qg", qg, (B, T, HV, K), bf), ("kg", kg, (B, T, HV, K), bf),
+                               ("w", w, (B, T, HV, K), bf), ("g2", g2, (B, T, HV, K), torch.float32),
+                               ("do", do, (B, T, HV, V), bf), ("dv", dv, (B, T, HV, V), bf),
+                               ("dht", dht, (N, HV, K, V), sdt), ("cu_seqlens", cu_seqlens, (N + 1,), torch.int64),
+                               ("dv2", dv2, (B, T, HV, V), bf), ("dh0", dh0, (N, HV, K, V), sdt)):
+        _check_tensor(name, t, shape, dt, dev)
+    _check_tensor("dhc", dhc, (C, HV, K, V), cdt, dev, min_rows=cu_seqlens is not None)
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be on a HIP device, they are on {dev}")
     if stream is None:
         stream = torch.cuda.current_stream(qg.device).cuda_stream
     a = KdaBwdDhuArgs()
@@ -298,7 +352,8 @@ def kda_bwd_dhu(qg, kg, w, g2, do, dv=None, dht=None, scale=None, cu_seqlens=Non
 
     Returns (dv2, dhc or None, dh0 or None): dv2 [B, T, HV, V] bf16, dhc [C, HV, K, V]
     (``checkpoint_dtype``: torch.float32 default, or torch.bfloat16) the gradient of
-    the state after each chunk (see ``num_chunks``), dh0 [N, HV, K, V] in
+    the state after each chunk (rows as hc of ``kda_fwd``: for varlen ``max_chunks`` rows,
+    of which sum_n ceil(len_n/64) are written), dh0 [N, HV, K, V] in
     ``state_dtype`` (torch.float32 default, or torch.bfloat16; dht must match).
     """
     import torch
@@ -317,8 +372,8 @@ def kda_bwd_dhu(qg, kg, w, g2, do, dv=None, dht=None, scale=None, cu_seqlens=Non
     dv2 = torch.empty((B, T, HV, V), dtype=torch.bfloat16, device=qg.device)
     dh0 = torch.empty((N, HV, K, V), dtype=sdt, device=qg.device) if output_dh0 else None
     dhc = None
-    if output_checkpoints:
-        dhc = torch.empty((num_chunks(T, cu_seqlens, B), HV, K, V), dtype=cdt, device=qg.device)
+    if output_checkpoints:   # varlen: room for the bound, no look at the lengths on the host
+        dhc = torch.empty((max_chunks(T, N, B, cu_seqlens is not None), HV, K, V), dtype=cdt, device=qg.device)
     args = make_bwd_args(qg, kg, w, g2, do, dv, dht, scale, cu_seqlens, dv2, dh0, dhc, flags=flags)
     n = kda_bwd_dhu_workspace_bytes(args)
     workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=qg.device)

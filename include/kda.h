@@ -62,8 +62,8 @@ typedef struct kda_fwd_args {
    *   q, k : [B, T, HQK, K]  keys/queries, expected L2-normalised over K by the caller
    *   v    : [B, T, HV,  V]
    *   g    : [B, T, HV,  K]  natural-log per-dimension decay, g <= 0; values
-   *          below -11, -inf included, are taken as -11 (a decay of 1.7e-5
-   *          instead of a smaller one: the outputs change by at most 1.7e-5 of the
+   *          below -10, -inf included, are taken as -10 (a decay of 4.5e-5
+   *          instead of a smaller one: the outputs change by at most 4.5e-5 of the
    *          state it multiplies); so is a NaN with its sign bit set
    *   beta : [B, T, HV]      write strength in [0, 1] (already through a sigmoid),
    *          or its logit with KDA_FLAG_BETA_LOGITS
@@ -103,8 +103,10 @@ typedef struct kda_fwd_args {
   /* Per-chunk states (kda_fwd / kda_fwd_inter), or NULL to skip them:
    *   hc : [C, HV, K, V] in the state dtype, the state *before* each chunk, chunks
    *        numbered sequence by sequence (sequence n's chunk j is chunk
-   *        sum_{m<n} ceil(len_m / 64) + j; fixed length: n * ceil(T/64) + j),
-   *        C = that total.  Alignment 16 bytes (fp32) or 8 bytes (bf16).
+   *        sum_{m<n} ceil(len_m / 64) + j; fixed length: n * ceil(T/64) + j).
+   *        C must be at least that total: B * ceil(T/64) for fixed length; for
+   *        varlen ceil(T/64) + N always suffices (rows past the total are not
+   *        written).  Alignment 16 bytes (fp32) or 8 bytes (bf16).
    * The chunked backward pass needs these (kernel-fun fwd_state module docstring,
    * which keeps h per chunk for the backward). */
   void* hc;
@@ -117,8 +119,11 @@ typedef struct kda_fwd_args {
 } kda_fwd_args;
 
 /* Workspace size for these arguments (host only, launches nothing).  Only the
- * shape fields (B, T, HQK, HV, K, V, N, and whether cu_seqlens is NULL) are
- * read.  Returns KDA_OK and *bytes, or an error status. */
+ * shape fields (B, T, HQK, HV, K, V, N, whether cu_seqlens is NULL) and seg_chunks
+ * are read.  With seg_chunks == 0 the size follows the state scan the library picks
+ * for the compute-unit count of the device current on the calling thread, so a
+ * workspace sized on one device kind fits calls made with that device current.
+ * Returns KDA_OK and *bytes, or an error status. */
 int kda_fwd_workspace_bytes(const kda_fwd_args* a, size_t* bytes);
 
 /* The state scan these arguments select (host only, launches nothing; reads the same
@@ -200,8 +205,8 @@ typedef struct kda_bwd_dhu_args {
   /* Outputs (device, caller-allocated).
    *   dv2 : bf16 [B, T, HV, V]  every row of every sequence is written
    *   dh0 : [N, HV, K, V] (dht's dtype), or NULL to skip
-   *   dhc : [C, HV, K, V] fp32 (bf16 with KDA_FLAG_CKPT_BF16), chunks numbered as
-   *         hc of kda_fwd_args, or NULL to skip
+   *   dhc : [C, HV, K, V] fp32 (bf16 with KDA_FLAG_CKPT_BF16), chunks numbered and
+   *         C sized as hc of kda_fwd_args, or NULL to skip
    * Alignment (else KDA_ERR_INVALID_ARG): qg, kg, w, g2, dht, dh0, dhc 16 bytes;
    * dout, dv, dv2 and cu_seqlens 8 bytes. */
   void* dv2;

@@ -24,15 +24,25 @@ def to_device(d, device="cuda"):
     return t
 
 
-def run_hip(d, dev=None, output_final_state=True, h0="from_inputs", workspace=None, o=None):
-    """Run kda_fwd on the inputs dict d; returns (o, ht) as float64 numpy."""
+def run_hip(d, dev=None, output_final_state=True, h0="from_inputs", workspace=None, o=None, nan_fill=True):
+    """Run kda_fwd on the inputs dict d; returns (o, ht) as float64 numpy.  With
+    ``nan_fill`` the outputs start as NaN, so that an element the kernels never write
+    cannot pass as a finite leftover."""
     import torch
     from gated_delta_rule_chunked_amd import kda_fwd
     t = dev if dev is not None else to_device(d)
     h = t["h0"] if h0 == "from_inputs" else h0
+    ht = None
+    if nan_fill:
+        if o is None:
+            o = torch.full(t["v"].shape, float("nan"), dtype=torch.bfloat16, device=t["v"].device)
+        if output_final_state:
+            N = t["q"].shape[0] if t["cu_seqlens"] is None else t["cu_seqlens"].numel() - 1
+            ht = torch.full((N, t["v"].shape[2], t["q"].shape[3], t["v"].shape[3]), float("nan"),
+                            dtype=torch.float32, device=t["v"].device)
     o_t, ht_t = kda_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=d["scale"], h0=h,
                         cu_seqlens=t["cu_seqlens"], output_final_state=output_final_state,
-                        workspace=workspace, o=o)
+                        workspace=workspace, o=o, ht=ht)
     torch.cuda.synchronize()
     o_np = o_t.float().cpu().numpy().astype(np.float64)
     ht_np = None if ht_t is None else ht_t.cpu().numpy().astype(np.float64)

@@ -77,7 +77,8 @@ def test_chunk_states_and_bf16_state_across_segments():
     _, _, inter = chunked(**{k: d[k] for k in FIELDS}, scale=d["scale"], h0=d["h0"],
                           cu_seqlens=d["cu_seqlens"], return_intermediates=True)
     hc_ref = np.stack([c["h"] for c in inter])
-    assert hc.shape == hc_ref.shape
+    assert hc.shape[0] >= hc_ref.shape[0]   # room for ceil(T/64) + N chunks
+    hc = hc[:hc_ref.shape[0]]
     assert nerr(hc, hc_ref) <= TOL
     o_ref, ht_ref = reference(d)
     assert nerr(o, o_ref) <= TOL and nerr(ht, ht_ref) <= TOL

@@ -407,22 +407,23 @@ def test_clean_copy_passes_pins():
 
 
 def test_gate_floor_changes_the_recurrence_by_less_than_its_decay():
-    """The GPU path raises per-token gates below -11 to -11.  In exact arithmetic
-    that changes the outputs by at most about exp(-11) = 1.7e-5 of the state
-    magnitude: checked here on the token recurrence with whole tokens, single
-    dimensions and -inf gates below the floor."""
+    """The GPU path raises per-token gates below -10 to -10.  In exact arithmetic
+    that changes the outputs by at most about exp(-10) = 4.5e-5 of the state
+    magnitude: checked here on the token recurrence with whole tokens, whole 16-token
+    blocks, single dimensions and -inf gates below the floor."""
     d = make_inputs(43, B=1, T=200, HQK=1, HV=2, K=32, V=16, has_h0=True)
     g = d["g"]
     g[0, 5, 0, :] = -30.0
     g[0, 63, 1, :] = -1000.0
     g[0, 64, 0, :] = -np.inf
     g[0, 70:90, 1, 3] = -np.inf
+    g[0, 100:116, 0, :] = -11.0
+    g[0, 120:137, 1, :10] = -np.inf
     g[0, 199, :, :] = -np.inf
     args = {k: d[k] for k in ("q", "k", "v", "beta")}
     o, ht = recurrent(**args, g=g, scale=d["scale"], h0=d["h0"])
-    o2, ht2 = recurrent(**args, g=np.maximum(g, -11.0), scale=d["scale"], h0=d["h0"])
+    o2, ht2 = recurrent(**args, g=np.maximum(g, -10.0), scale=d["scale"], h0=d["h0"])
     assert np.isfinite(o).all() and np.isfinite(ht).all()
     smax = max(np.abs(ht).max(), np.abs(d["h0"]).max())
-    assert np.abs(o2 - o).max() < 2e-5 * smax
-    assert np.abs(ht2 - ht).max() < 2e-5 * smax
-
+    assert np.abs(o2 - o).max() < 5e-5 * smax
+    assert np.abs(ht2 - ht).max() < 5e-5 * smax
