@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "../../include/kda.h"
 #include "kda_device.hpp"
@@ -25,6 +26,12 @@ static_assert(offsetof(kda_bwd_dhu_args, scale) == 56 && offsetof(kda_bwd_dhu_ar
 static_assert(kda::FLAG_BETA_LOGITS == KDA_FLAG_BETA_LOGITS && kda::FLAG_STATE_BF16 == KDA_FLAG_STATE_BF16 &&
                   kda::FLAG_CKPT_BF16 == KDA_FLAG_CKPT_BF16,
               "flag bits match the public header");
+
+// Scratch of kda_fwd_no_alloc: one static array per device the library runs on, held
+// until the process ends.  In host code `scratch` names a host-side stand-in, not a
+// device address: kernels and copies get the address looked up by
+// hipGetSymbolAddress on the device in question (scratch_on_current_device).
+static __device__ __attribute__((aligned(256))) uint8_t scratch[KDA_NO_ALLOC_MAX_BYTES];
 
 namespace {
 
@@ -197,6 +204,29 @@ int check_bwd_shapes(const kda_bwd_dhu_args* a, int64_t* ws_bytes) {
   return KDA_OK;
 }
 
+// Device address of `scratch` on the current device, looked up once per device (the
+// first call on a device makes it; concurrent first calls look up the same address).
+constexpr int MAX_DEVICES = 64;
+std::atomic<uint8_t*> g_scratch[MAX_DEVICES];
+
+int scratch_on_current_device(uint8_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= MAX_DEVICES) return KDA_ERR_UNSUPPORTED;
+  uint8_t* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    void* sym = nullptr;
+    e = hipGetSymbolAddress(&sym, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (sym == nullptr || !aligned(sym, 256)) return KDA_ERR_WORKSPACE;
+    ptr = static_cast<uint8_t*>(sym);
+    g_scratch[dev].store(ptr, std::memory_order_release);
+  }
+  *out = ptr;
+  return KDA_OK;
+}
+
 int run_intra(const kda::Params& p, hipStream_t s) {
   if (p.max_chunks * p.HV == 0) return KDA_OK;
   int st = hip_status(p.cu ? kda::launch_chunk_table(p.cu, p.N, p.T, p.max_chunks, p.table, p.counter, p.seg_L,
@@ -249,6 +279,21 @@ int kda_fwd(const kda_fwd_args* a) {
   st = run_intra(p, (hipStream_t)a->stream);
   if (st != KDA_OK) return st;
   return hip_status(p.seg_path ? kda::launch_scan(p, (hipStream_t)a->stream) : kda::launch_inter(p, (hipStream_t)a->stream));
+}
+
+int kda_fwd_no_alloc(const kda_fwd_args* a) {
+  if (!a) return KDA_ERR_INVALID_ARG;
+  kda::WsLayout L;
+  int st = check_shapes(a, &L);
+  if (st != KDA_OK) return st;
+  if ((uint64_t)L.total_bytes > (uint64_t)KDA_NO_ALLOC_MAX_BYTES) return KDA_ERR_TOO_LARGE;
+  uint8_t* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st != KDA_OK) return st;
+  kda_fwd_args b = *a;
+  b.workspace = ws;
+  b.workspace_bytes = KDA_NO_ALLOC_MAX_BYTES;
+  return kda_fwd(&b);
 }
 
 int kda_debug_unpack(const kda_fwd_args* a, void* qg, void* w, void* kg, void* aqk, void* tmb,
@@ -322,6 +367,9 @@ const char* kda_strerror(int status) {
     case KDA_ERR_UNSUPPORTED: return "unsupported shape (K must be 64 or 128, V a positive multiple of 16)";
     case KDA_ERR_WORKSPACE: return "workspace missing, not 256-byte aligned, or smaller than kda_fwd_workspace_bytes";
     case KDA_ERR_HIP: return g_hip_msg;
+    case KDA_ERR_TOO_LARGE:
+      return "the shapes need more scratch than kda_fwd_no_alloc's static buffer (KDA_NO_ALLOC_MAX_BYTES) holds; "
+             "call kda_fwd with a workspace";
     default: return "unknown status";
   }
 }

@@ -19,13 +19,15 @@ KDA_ERR_INVALID_ARG = -1
 KDA_ERR_UNSUPPORTED = -2
 KDA_ERR_WORKSPACE = -3
 KDA_ERR_HIP = -4
+KDA_ERR_TOO_LARGE = -5
+KDA_NO_ALLOC_MAX_BYTES = 128 << 20
 KDA_CHUNK = 64
 KDA_FLAG_BETA_LOGITS = 1
 KDA_FLAG_STATE_BF16 = 2
 KDA_FLAG_CKPT_BF16 = 4
 
-EXPORTED = ("kda_fwd_workspace_bytes", "kda_fwd_scan_plan", "kda_fwd", "kda_fwd_intra", "kda_fwd_inter",
-            "kda_debug_unpack", "kda_bwd_dhu_workspace_bytes", "kda_bwd_dhu", "kda_strerror")
+EXPORTED = ("kda_fwd_workspace_bytes", "kda_fwd_scan_plan", "kda_fwd", "kda_fwd_no_alloc", "kda_fwd_intra",
+            "kda_fwd_inter", "kda_debug_unpack", "kda_bwd_dhu_workspace_bytes", "kda_bwd_dhu", "kda_strerror")
 
 
 class KdaFwdArgs(ctypes.Structure):
@@ -75,7 +77,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     P = ctypes.POINTER(KdaFwdArgs)
     lib.kda_fwd_workspace_bytes.argtypes = [P, ctypes.POINTER(c_size_t)]
-    for name in ("kda_fwd", "kda_fwd_intra", "kda_fwd_inter"):
+    for name in ("kda_fwd", "kda_fwd_no_alloc", "kda_fwd_intra", "kda_fwd_inter"):
         getattr(lib, name).argtypes = [P]
         getattr(lib, name).restype = c_int
     lib.kda_fwd_workspace_bytes.restype = c_int
@@ -206,6 +208,13 @@ def _call(name: str, args: KdaFwdArgs) -> None:
 
 def kda_fwd_raw(args: KdaFwdArgs) -> None:
     _call("kda_fwd", args)
+
+
+def kda_fwd_no_alloc_raw(args: KdaFwdArgs) -> None:
+    """kda_fwd on the library's static per-device scratch (``args.workspace`` is
+    ignored); raises KdaError with KDA_ERR_TOO_LARGE when the shapes need more than
+    KDA_NO_ALLOC_MAX_BYTES."""
+    _call("kda_fwd_no_alloc", args)
 
 
 def kda_fwd_intra(args: KdaFwdArgs) -> None:

@@ -44,6 +44,8 @@ extern "C" {
 #define KDA_ERR_UNSUPPORTED   -2  /* K not in {64, 128}, V not a multiple of 16           */
 #define KDA_ERR_WORKSPACE     -3  /* workspace NULL, misaligned or smaller than required  */
 #define KDA_ERR_HIP           -4  /* a HIP launch failed; see kda_strerror                */
+#define KDA_ERR_TOO_LARGE     -5  /* kda_fwd_no_alloc: the shapes need more scratch than
+                                     KDA_NO_ALLOC_MAX_BYTES                                */
 
 /* Chunk length of the chunked form (tokens per chunk). */
 #define KDA_CHUNK 64
@@ -118,6 +120,10 @@ typedef struct kda_fwd_args {
   int32_t seg_chunks;
 } kda_fwd_args;
 
+/* Largest workspace kda_fwd_no_alloc can use: the size of the library's static
+ * per-device scratch buffer. */
+#define KDA_NO_ALLOC_MAX_BYTES ((size_t)128 << 20)
+
 /* Workspace size for these arguments (host only, launches nothing).  Only the
  * shape fields (B, T, HQK, HV, K, V, N, whether cu_seqlens is NULL) and seg_chunks
  * are read.  With seg_chunks == 0 the size follows the state scan the library picks
@@ -142,6 +148,21 @@ int kda_fwd_scan_plan(const kda_fwd_args* a, int32_t* seg_chunks);
  * docstring; FlashKDA recurrence phases 3-6).  Equivalent to kda_fwd_intra
  * followed by kda_fwd_inter on the same stream. */
 int kda_fwd(const kda_fwd_args* a);
+
+/* kda_fwd without a caller workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same kernels and results as kda_fwd; a->workspace and
+ * a->workspace_bytes are ignored.  The scratch is a static device array of
+ * KDA_NO_ALLOC_MAX_BYTES that the library holds on every device it runs on until the
+ * process ends; its address is looked up on the first call on each device.  The call
+ * allocates nothing: shapes whose kda_fwd_workspace_bytes exceeds
+ * KDA_NO_ALLOC_MAX_BYTES are rejected with KDA_ERR_TOO_LARGE before any launch (at
+ * K = V = 128 about 2,000 (chunk, value head) pairs fit, e.g. 4,096 tokens x 32
+ * heads).  Every call on one device shares that device's buffer: calls that overlap
+ * in time on one device (different streams, or threads) race and must not be made;
+ * calls in stream order are safe, since each call rewrites every byte it reads (the
+ * work counter and chunk tables are reset by the call's first kernel). */
+int kda_fwd_no_alloc(const kda_fwd_args* a);
 
 /* Intra-chunk stage only (per-dimension gate cumsum, gated Aqk, Akk and its
  * UT/WY inverse, w, qg, kg; kernel-fun docstring): fills the workspace from

@@ -242,3 +242,14 @@ def test_bwd_workspace_bytes(lib):
 def test_bwd_validation_rejects_before_launch(lib, over, status):
     assert lib.kda_bwd_dhu(ctypes.byref(bwd_args(**over))) == status
     assert lib.kda_bwd_dhu(None) == K.KDA_ERR_INVALID_ARG
+
+
+def test_no_alloc_rejects_shapes_beyond_its_static_buffer(lib):
+    # the 8192-token, 32-head workload needs about 270 MB of workspace, more than the
+    # static scratch of kda_fwd_no_alloc holds: refused before any device call
+    a = args(B=1, T=8192, HQK=32, HV=32)
+    st, n = ws(a)
+    assert st == 0 and n > K.KDA_NO_ALLOC_MAX_BYTES
+    assert lib.kda_fwd_no_alloc(ctypes.byref(a)) == K.KDA_ERR_TOO_LARGE
+    assert "KDA_NO_ALLOC_MAX_BYTES" in K.kda_strerror(K.KDA_ERR_TOO_LARGE)
+    assert lib.kda_fwd_no_alloc(None) == K.KDA_ERR_INVALID_ARG
