@@ -17,7 +17,8 @@
 static_assert(offsetof(kda_fwd_args, scale) == 40 && offsetof(kda_fwd_args, B) == 64 &&
                   offsetof(kda_fwd_args, o) == 96 && offsetof(kda_fwd_args, stream) == 128 &&
                   offsetof(kda_fwd_args, flags) == 136 && offsetof(kda_fwd_args, hc) == 144 &&
-                  offsetof(kda_fwd_args, seg_chunks) == 152 && sizeof(kda_fwd_args) == 160,
+                  offsetof(kda_fwd_args, seg_chunks) == 152 && offsetof(kda_fwd_args, chunk) == 156 &&
+                  sizeof(kda_fwd_args) == 160,
               "argument struct layout (mirrored by the Python binding)");
 static_assert(offsetof(kda_bwd_dhu_args, scale) == 56 && offsetof(kda_bwd_dhu_args, B) == 72 &&
                   offsetof(kda_bwd_dhu_args, dv2) == 96 && offsetof(kda_bwd_dhu_args, stream) == 136 &&
@@ -54,6 +55,7 @@ int check_shapes(const kda_fwd_args* a, kda::WsLayout* L) {
   if (a->B < 1 || a->T < 0 || a->HQK < 1 || a->HV < 1 || a->N < 1) return KDA_ERR_INVALID_ARG;
   if (a->HV % a->HQK != 0) return KDA_ERR_INVALID_ARG;
   if (a->seg_chunks < 0) return KDA_ERR_INVALID_ARG;
+  if (a->chunk != 0 && a->chunk != 64 && a->chunk != 16) return KDA_ERR_UNSUPPORTED;
   if (a->cu_seqlens) {
     if (a->B != 1) return KDA_ERR_INVALID_ARG;
   } else if (a->N != a->B) {
@@ -69,8 +71,11 @@ int check_shapes(const kda_fwd_args* a, kda::WsLayout* L) {
   if (units16 >= ((int64_t)1 << 31) - 8) return KDA_ERR_INVALID_ARG;
   if (a->N >= (1 << 30)) return KDA_ERR_INVALID_ARG;
   // scan choice and segment plan
-  const kda::ScanPlan plan = kda::choose_scan(nt, a->cu_seqlens != nullptr, a->N, a->HV, a->V,
-                                              a->seg_chunks > 0 ? 0 : kda::device_cus(), a->seg_chunks);
+  kda::ScanPlan plan = kda::choose_scan(nt, a->cu_seqlens != nullptr, a->N, a->HV, a->V,
+                                        a->seg_chunks > 0 ? 0 : kda::device_cus(), a->seg_chunks);
+  // chunk 16 runs on the 64-column scan only: where the serial scan would be chosen,
+  // one segment per sequence
+  if (a->chunk == 16 && !plan.seg_path) plan = {true, std::max<int64_t>(nt, 1)};
   const bool seg_path = plan.seg_path;
   int64_t seg_L = plan.seg_L;
   seg_L = std::min<int64_t>(seg_L, std::max<int64_t>(nt, 1));
@@ -136,6 +141,7 @@ int check_call(const kda_fwd_args* a, int need, kda::Params* p) {
       return KDA_ERR_INVALID_ARG;
   }
   if (!aligned(a->cu_seqlens, 8) || !aligned(a->hc, 16)) return KDA_ERR_INVALID_ARG;
+  if (a->chunk == 16 && a->hc) return KDA_ERR_UNSUPPORTED;
   if (a->flags & ~(uint32_t)(KDA_FLAG_BETA_LOGITS | KDA_FLAG_STATE_BF16)) return KDA_ERR_INVALID_ARG;
   if (L.total_bytes > 0) {
     if (!a->workspace || !aligned(a->workspace, 256)) return KDA_ERR_WORKSPACE;
@@ -153,6 +159,7 @@ int check_call(const kda_fwd_args* a, int need, kda::Params* p) {
   p->ht = a->ht;
   p->hc = a->hc;
   p->flags = a->flags;
+  p->c16 = a->chunk == 16;
   uint8_t* ws = (uint8_t*)a->workspace;
   p->counter = (int32_t*)ws;
   p->table = a->cu_seqlens ? (int32_t*)(ws + 16) : nullptr;
@@ -301,6 +308,7 @@ int kda_debug_unpack(const kda_fwd_args* a, void* qg, void* w, void* kg, void* a
   kda::Params p;
   int st = check_call(a, 0, &p);
   if (st != KDA_OK) return st;
+  if (p.c16) return KDA_ERR_UNSUPPORTED;   // the unpacked layout is that of chunk 64
   const void* outs[] = {qg, w, kg, aqk, tmb, alpha};
   for (const void* ptr : outs)
     if (!aligned(ptr, 16)) return KDA_ERR_INVALID_ARG;

@@ -26,6 +26,11 @@ typedef __bf16 bf16x2n __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ f32x4 mfma16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// v_mfma_f32_16x16x16_bf16: A lane holds A[r][4g .. 4g+3], B lane holds B[4g .. 4g+3][r]
+// (either half of a P-order 32-step fragment, or a packed C-layout tile as B).
+__device__ __forceinline__ f32x4 mfma16x16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
 // v_mfma_f32_16x16x4_f32 (fp32 operands): A lane holds A[r][g], B lane holds
 // B[g][r], C as above.
 __device__ __forceinline__ f32x4 mfma16x4f32(float a, float b, f32x4 c) {
@@ -139,6 +144,7 @@ __device__ __forceinline__ uint2 pack4(const f32x4& a) {
 __device__ __forceinline__ bf16x8 cat(const uint2& lo, const uint2& hi) {
   return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
+__device__ __forceinline__ bf16x4 as_half(const uint2& u) { return __builtin_bit_cast(bf16x4, u); }
 __device__ __forceinline__ uint2 lds8(const uint8_t* p) { return *reinterpret_cast<const uint2*>(p); }
 __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
@@ -204,6 +210,19 @@ struct Rec {
   static constexpr int BYTES = AQK + 6 * 1024;     // 61952 (K=128), 37120 (K=64)
   static_assert(BYTES % 256 == 0 && STATE_BYTES % 256 == 0, "records stay 256-byte aligned");
 };
+// Chunk 16 (FlashKDA's chunk length) uses the same records: one per 64 rows, holding
+// four 16-row chunks whose Aqk and Tm diag(beta) are block diagonal, so fragments
+// (2,0) and (3,0) of AQK and TMB are zero and never read.  The decay rows exp2(G) of
+// sub-chunks 1..3 live in those two TMB fragments (part of the state block, so the
+// state pass stages them); sub-chunk 0's is the ALPHA row.
+template <int K>
+__device__ __host__ __forceinline__ constexpr int alpha16_off(int I) {
+  return I == 0 ? Rec<K>::ALPHA
+                : Rec<K>::TMB + (((I - 1) * K) / 256 == 0 ? 2 : 4) * 1024 + (((I - 1) * K) % 256) * 4;
+}
+static_assert(alpha16_off<128>(3) + 128 * 4 <= Rec<128>::TMB + 5 * 1024 && alpha16_off<64>(3) + 64 * 4 <= Rec<64>::TMB + 3 * 1024,
+              "chunk-16 decay rows stay inside the zero TMB fragments");
+
 // Records are stored chunk-major: the HV records of one chunk are contiguous.
 // The scans run consecutive heads side by side at the same chunk position, so
 // the records in flight at one time sit next to each other instead of being

@@ -360,6 +360,7 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void inter_kernel(Params p, int n
 }
 
 hipError_t launch_inter(const Params& p, hipStream_t s) {
+  if (p.c16) return hipErrorInvalidValue;   // chunk 16 runs on the 64-column scan (kda_plan.hpp choice)
   const int64_t items = (int64_t)p.N * p.HV * (p.V / BV);
   if (items == 0) return hipSuccess;
   // longest-first order: whole rounds of eight units, V / 16 workgroups each

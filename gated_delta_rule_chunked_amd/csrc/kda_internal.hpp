@@ -29,6 +29,7 @@ struct Params {
   uint8_t* recs;         // workspace records
   float scale;
   uint32_t flags;        // KDA_FLAG_* bits
+  bool c16;              // chunk length 16 (four 16-row chunks per 64-row record), else 64
   int B, T, HQK, HV, K, V, N;
   int NT;                // fixed length: chunks per sequence
   int64_t max_chunks;    // workspace capacity in chunks (per value head)

@@ -28,6 +28,11 @@
 // exp(Gam_i) = X_i exp(mu_I), exp(Gam_last - Gam_i) = Y_i exp(Gam_last - mu_I); where
 // one of those second factors underflows the product is below exp(-12) as well.
 //
+// Chunk 16 (C16): the 64 rows of an item are four chunks of 16.  Only the diagonal
+// blocks of Aqk, Akk and Tm exist, every Gam-referenced factor is taken relative to
+// its 16-row chunk (exp(Gam_i - P_I) = X_i exp(tot_I / 2), exp(P_{I+1} - Gam_i) =
+// Y_i exp(tot_I / 2)), and each 16-row chunk gets its own decay row exp(tot_I).
+//
 // Wave I owns rows 16I..16I+15 through the gate phase (the Aqk/Akk blocks are then
 // shared out evenly, see phase 2); lane
 // l = 16g + r holds row 16I + r and the P-order key dims 32s + pidx(g, e)
@@ -216,7 +221,7 @@ __device__ __forceinline__ uint32_t gate_floor2(uint32_t w) {
 #ifndef KDA_INTRA_OCC
 #define KDA_INTRA_OCC 2   // workgroups per CU the register budget is sized for
 #endif
-template <int K>
+template <int K, bool C16>
 __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p, int n_items,
                                                                          const int32_t* __restrict__ tbl,
                                                                          const int2* __restrict__ cinfo) {
@@ -363,7 +368,9 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
   //   rows 4..7   F_I = exp(Gam_last - mu_I)
   //   rows 8..13  c_IJ = exp(mu_I - P_{J+1}), pair (I,J) -> 8 + I(I-1)/2 + J
   //   rows 14..16 H_J = exp(tot_J / 2), so that Y_j H_J = exp(P_{J+1} - Gam_j)
-  // every argument is <= 0 except the midpoint offsets folded into X and Y
+  // every argument is <= 0 except the midpoint offsets folded into X and Y.  Chunk 16:
+  // rows 0..7 are exp(tot_I / 2) (the gate restarts at every 16-row chunk), rows 8..16
+  // are not read, and each 16-row chunk's decay row exp(tot_I) is stored.
   {
     constexpr int STEP = NTHREADS / K;            // table rows per pass (2 or 4)
     const int d = tid % K, r0 = tid / K;          // r0 is uniform over a wave (64 divides K)
@@ -371,13 +378,22 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
     const float m0 = 0.5f * t0, m1 = t0 + 0.5f * t1, m2 = t0 + t1 + 0.5f * t2, m3 = t0 + t1 + t2 + 0.5f * t3;
     const float P1 = t0, P2 = t0 + t1, P3 = t0 + t1 + t2;
     const float G = t0 + t1 + t2 + t3;
-    const float arg[SM::NTAB] = {m0, m1, m2, m3, G - m0, G - m1, G - m2, G - m3,
+    const float h0 = 0.5f * t0, h1 = 0.5f * t1, h2 = 0.5f * t2, h3 = 0.5f * t3;
+    const float arg[SM::NTAB] = {C16 ? h0 : m0, C16 ? h1 : m1, C16 ? h2 : m2, C16 ? h3 : m3,
+                                 C16 ? h0 : G - m0, C16 ? h1 : G - m1, C16 ? h2 : G - m2, C16 ? h3 : G - m3,
                                  m1 - P1, m2 - P1, m2 - P2, m3 - P1, m3 - P2, m3 - P3,
-                                 0.5f * t0, 0.5f * t1, 0.5f * t2};
+                                 h0, h1, h2};
 #pragma unroll
     for (int row = 0; row < SM::NTAB; ++row)
       if (row % STEP == r0) sTab[row * K + d] = __builtin_amdgcn_exp2f(LOG2E * arg[row]);
-    if (r0 == 0) reinterpret_cast<float*>(rec + R::ALPHA)[d] = __builtin_amdgcn_exp2f(LOG2E * G);
+    if (C16) {
+      const float tt[4] = {t0, t1, t2, t3};
+#pragma unroll
+      for (int J = 0; J < 4; ++J)
+        if (J % STEP == r0) reinterpret_cast<float*>(rec + alpha16_off<K>(J))[d] = __builtin_amdgcn_exp2f(LOG2E * tt[J]);
+    } else if (r0 == 0) {
+      reinterpret_cast<float*>(rec + R::ALPHA)[d] = __builtin_amdgcn_exp2f(LOG2E * G);
+    }
   }
   __syncthreads();  // B2: tables
 
@@ -481,7 +497,8 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
     for (int h = 0; h < 2; ++h) {
       const int J = 2 * s2 + h;
       f32x4 aq = f32x4{0.f, 0.f, 0.f, 0.f}, ak = aq;
-      if (J <= Ib) {
+      const bool cross = !C16 && J < Ib;   // chunk 16: only the diagonal blocks exist
+      if (J == Ib || cross) {
         const int pr = 8 + Ib * (Ib - 1) / 2 + J;   // c_IJ table row (J < Ib)
 #pragma unroll
         for (int s = 0; s < S; ++s) {
@@ -507,8 +524,8 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int j = 4 * g + rr;   // column within block J
-        vq[h][rr] = (J < Ib || (J == Ib && j <= r)) ? p.scale * aq[rr] : 0.f;
-        vko[h][rr] = (J < Ib || (J == Ib && j < r)) ? -bti * ak[rr] : 0.f;   // -Akk
+        vq[h][rr] = (cross || (J == Ib && j <= r)) ? p.scale * aq[rr] : 0.f;
+        vko[h][rr] = (cross || (J == Ib && j < r)) ? -bti * ak[rr] : 0.f;   // -Akk
       }
     }
     store_stream(rec + R::AQK + (tri_frag(Ib, s2) * 64 + ln) * 16, pack_pair(vq[0], vq[1]));
@@ -594,10 +611,11 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
   //     16x16x16 products as four fp32 MFMAs; step kb takes contraction index
   //     4g + kb in lane group g, so a C-layout result feeds the next product's B
   //     operand straight from its registers.
+  //     Chunk 16: Akk is block diagonal, so these blocks are zero and stay zero in LDS.
   f32x4 inv[4];
 #pragma unroll
   for (int M = 0; M < 4; ++M) inv[M] = f32x4{0.f, 0.f, 0.f, 0.f};
-  {
+  if (!C16) {
     const int J = I;
 #pragma unroll
     for (int M = 1; M < 4; ++M) {
@@ -625,17 +643,19 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
   __syncthreads();  // B7: every read of the Akk blocks is done
 #pragma unroll
   for (int M = 1; M < 4; ++M) {
-    if (M <= I) continue;
+    if (C16 || M <= I) continue;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) sAkk[(16 * M + 4 * g + rr) * SM::AS + 16 * I + r] = inv[M][rr];
   }
   __syncthreads();  // B8: Tm complete
 
   // ---- phase 4: TmB = Tm diag(beta) fragments; w^T = (k exp(Gam))^T TmB^T ----------
+  // Chunk 16: fragment (I, 0) of row blocks 2 and 3 is zero (block diagonal); its record
+  // slot holds the decay rows instead, and its products are skipped.
   bf16x8 TBn[2];   // -TmB: the w products then leave -w, the WN record, directly
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2) {
-    if (s2 >= tri_steps(I)) continue;
+    if (s2 >= tri_steps(I) || (C16 && I >= 2 && s2 == 0)) continue;
     const float* trow = sAkk + i * SM::AS + 32 * s2;
     const float* brow = sBeta + 32 * s2;
     const float4 t0 = *reinterpret_cast<const float4*>(trow + 4 * g);
@@ -658,7 +678,7 @@ __global__ __launch_bounds__(NTHREADS, KDA_INTRA_OCC) void intra_kernel(Params p
       acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        if (s2 >= tri_steps(I)) continue;
+        if (s2 >= tri_steps(I) || (C16 && I >= 2 && s2 == 0)) continue;
         acc[h] = mfma16x32(as_frag(kt_frag(32 * s2, 16 * (2 * s + h), SM::KDT - SM::KT)), TBn[s2], acc[h]);
       }
     }
@@ -770,8 +790,14 @@ hipError_t launch_intra(const Params& p, hipStream_t s) {
   if (items == 0) return hipSuccess;
   // persistent grid: KDA_INTRA_OCC resident workgroups per CU, each looping over items
   const int grid = padded8(std::min<int64_t>(items, (int64_t)device_cus() * KDA_INTRA_OCC));
-  if (p.K == 128) hipLaunchKernelGGL(intra_kernel<128>, dim3(grid), dim3(NTHREADS), 0, s, p, (int)items, p.table, p.cinfo);
-  else hipLaunchKernelGGL(intra_kernel<64>, dim3(grid), dim3(NTHREADS), 0, s, p, (int)items, p.table, p.cinfo);
+  const dim3 gd(grid), bd(NTHREADS);
+  if (p.K == 128) {
+    if (p.c16) hipLaunchKernelGGL((intra_kernel<128, true>), gd, bd, 0, s, p, (int)items, p.table, p.cinfo);
+    else hipLaunchKernelGGL((intra_kernel<128, false>), gd, bd, 0, s, p, (int)items, p.table, p.cinfo);
+  } else {
+    if (p.c16) hipLaunchKernelGGL((intra_kernel<64, true>), gd, bd, 0, s, p, (int)items, p.table, p.cinfo);
+    else hipLaunchKernelGGL((intra_kernel<64, false>), gd, bd, 0, s, p, (int)items, p.table, p.cinfo);
+  }
   return hipGetLastError();
 }
 

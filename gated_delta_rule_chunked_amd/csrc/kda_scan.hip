@@ -41,6 +41,12 @@
 //     the full pass, half of the state part in the state pass) goes into that slot
 //     directly, by LDS-DMA loads issued as chunk c starts.
 
+// Chunk 16 (C16): every 64-row record holds four 16-row chunks (block-diagonal TmB and
+// Aqk, one decay row per 16-row chunk, kda_device.hpp).  The column waves then run four
+// state updates per staged record: for 16-row chunk I, v'_I = u_I + (-w_I) h,
+// o_I = qg_I h + Aqk_II v'_I and h <- diag(alpha_I) h + kg_I^T v'_I, the last two
+// contracting over 16 tokens with the 16x16x16 MFMA on one half of a record fragment.
+
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
@@ -129,7 +135,7 @@ __device__ __forceinline__ bool locate_segment(const Params& p, int64_t sigma, S
 // column waves.  Waves from `lwave0` on are the loader waves; column wave cw is wave
 // `cwave0` + cw (the state pass runs the b and M column waves of a group in one
 // workgroup, each set through its own instantiation, over one set of loaders).
-template <int K, int MODE>
+template <int K, int MODE, bool C16>
 __device__ __forceinline__ void scan_body(const Params& p, uint8_t* smem, const SegLoc& sl, int hv, int grp,
                                           int ntiles, int64_t sigma, int lwave0 = 4, int cwave0 = 0) {
   using SM = ScanSmem<K, MODE>;
@@ -330,7 +336,7 @@ __device__ __forceinline__ void scan_body(const Params& p, uint8_t* smem, const 
     if (MODE == SCAN_FULL && ph >= 1 && ph <= ncs) store_o(ph - 1);
     if (ph < ncs) {
       const int c = sl.c0 + ph;
-      if (MODE == SCAN_FULL && p.hc) {   // the state before this chunk
+      if (MODE == SCAN_FULL && !C16 && p.hc) {   // the state before this chunk
         // the row stride is re-made opaque every chunk, so the 32 row offsets stay
         // transient scalars instead of being hoisted as live 64-bit addresses
         int sv = p.V;
@@ -351,6 +357,79 @@ __device__ __forceinline__ void scan_body(const Params& p, uint8_t* smem, const 
         }
       }
       const uint8_t* st = smem + (ph & 1) * SM::SLOT;
+      if constexpr (C16) {
+        // ---- four 16-row chunks per record ----
+        // u = TmB v with TmB block diagonal: row block mb needs only the fragment that
+        // holds its diagonal block, (0,0) (1,0) (2,1) (3,1)
+        f32x4 u[4];
+        if (MODE != SCAN_M) {
+          const uint8_t* vt = smem + SM::VT + ((ph & 1) * 4 + cw) * SM::VT_BYTES + tr16;
+          const bf16x8 vb0 = cat(lds_tr8(vt), lds_tr8(vt + 16 * BV * 2));
+          const bf16x8 vb1 = cat(lds_tr8(vt + 32 * BV * 2), lds_tr8(vt + 48 * BV * 2));
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+            u[mb] = mfma16x32(as_frag(lds16(st + R::TMB + (tri_frag(mb, mb >> 1) * 64 + ln) * 16)), mb < 2 ? vb0 : vb1,
+                              f32x4{0.f, 0.f, 0.f, 0.f});
+        } else {
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) u[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        uint2 ov[4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+          // operands of 16-row chunk I: its decay row, the -w rows, the halves of the kg^T
+          // fragments that cover its tokens
+          float4 al[ND];
+          uint4 wn[S];
+          uint2 kgh[ND];
+#pragma unroll
+          for (int md = 0; md < ND; ++md)
+            al[md] = *reinterpret_cast<const float4*>(st + alpha16_off<K>(I) + (16 * md + 4 * g) * 4);
+#pragma unroll
+          for (int s = 0; s < S; ++s) wn[s] = lds16(st + R::WN + ((I * S + s) * 64 + ln) * 16);
+#pragma unroll
+          for (int md = 0; md < ND; ++md)
+            kgh[md] = lds8(st + R::KGT + ((2 * md + (I >> 1)) * 64 + ln) * 16 + (I & 1) * 8);
+          __builtin_amdgcn_sched_barrier(0);
+          uint2 hb[ND];
+#pragma unroll
+          for (int md = 0; md < ND; ++md) {
+            hb[md] = pack4(h[md]);
+            h[md][0] *= al[md].x;
+            h[md][1] *= al[md].y;
+            h[md][2] *= al[md].z;
+            h[md][3] *= al[md].w;
+          }
+          // v'_I = u_I + (-w_I) h
+          f32x4 acc = u[I];
+#pragma unroll
+          for (int s = 0; s < S; ++s) acc = mfma16x32(as_frag(wn[s]), cat(hb[2 * s], hb[2 * s + 1]), acc);
+          const uint2 vp = pack4(acc);
+          // h <- diag(alpha_I) h + kg_I^T v'_I  (16 tokens: one 16x16x16 product per tile)
+#pragma unroll
+          for (int md = 0; md < ND; ++md) h[md] = mfma16x16(as_half(kgh[md]), as_half(vp), h[md]);
+          if (MODE == SCAN_FULL) {
+            // o_I^T = h^T qg_I^T + v'_I^T Aqk_II^T: h before this 16-row chunk
+            uint4 qg[S];
+#pragma unroll
+            for (int s = 0; s < S; ++s) qg[s] = lds16(st + R::QG + ((I * S + s) * 64 + ln) * 16);
+            const uint2 aqh = lds8(st + R::AQK + (tri_frag(I, I >> 1) * 64 + ln) * 16 + (I & 1) * 8);
+            f32x4 oacc = f32x4{0.f, 0.f, 0.f, 0.f}, oacc2 = oacc;
+#pragma unroll
+            for (int s = 0; s < S; s += 2) {
+              oacc = mfma16x32(cat(hb[2 * s], hb[2 * s + 1]), as_frag(qg[s]), oacc);
+              oacc2 = mfma16x32(cat(hb[2 * s + 2], hb[2 * s + 3]), as_frag(qg[s + 1]), oacc2);
+            }
+            oacc = mfma16x16(as_half(vp), as_half(aqh), oacc);
+            ov[I] = pack4(oacc + oacc2);
+          }
+        }
+        if (MODE == SCAN_FULL) {
+          uint8_t* ob = smem + SM::OST + (ph & 1) * SM::OST_BYTES + (16 * cw + 4 * g) * 2;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) *reinterpret_cast<uint2*>(ob + (16 * w + r) * SM::OSTR) = ov[w];
+        }
+      } else {
       // batch 1: v^T fragments, TmB, decay, -w (in the order they are consumed)
       bf16x8 vb0, vb1;
       uint4 tm[6];
@@ -453,6 +532,7 @@ __device__ __forceinline__ void scan_body(const Params& p, uint8_t* smem, const 
 #pragma unroll
         for (int w = 0; w < 4; ++w) *reinterpret_cast<uint2*>(ob + (16 * w + r) * SM::OSTR) = ov[w];
       }
+      }   // chunk 64
     }
     barrier_lds();
   }
@@ -493,7 +573,7 @@ __device__ __forceinline__ void scan_body(const Params& p, uint8_t* smem, const 
 // M in separate workgroups the benchmarked shape needed 320 of them, a second round on
 // 256 compute units; paired they are 192.
 constexpr int SCAN_STATE_THREADS = 768;
-template <int K>
+template <int K, bool C16>
 __global__ __launch_bounds__(SCAN_STATE_THREADS, 1) void scan_state_kernel(Params p, int n_items) {
   static_assert(ScanSmem<K, SCAN_B>::SLOT == ScanSmem<K, SCAN_M>::SLOT, "b and M waves read one staging layout");
   __shared__ __attribute__((aligned(16))) uint8_t smem[ScanSmem<K, SCAN_B>::BYTES];
@@ -512,13 +592,13 @@ __global__ __launch_bounds__(SCAN_STATE_THREADS, 1) void scan_state_kernel(Param
   if (nb == 0 && nm == 0) return;                         // uniform over the workgroup
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave >= 4 && wave < 8)
-    scan_body<K, SCAN_M>(p, smem, sl, hv, j, nm, sigma, 8, 4);
+    scan_body<K, SCAN_M, C16>(p, smem, sl, hv, j, nm, sigma, 8, 4);
   else   // b column waves and the loaders (which also stage v for the b waves)
-    scan_body<K, SCAN_B>(p, smem, sl, hv, j, nb, sigma, 8, 0);
+    scan_body<K, SCAN_B, C16>(p, smem, sl, hv, j, nb, sigma, 8, 0);
 }
 
 // Full pass: item = (sigma * HV + hv) * NCG + cg.
-template <int K>
+template <int K, bool C16>
 __global__ __launch_bounds__(SCAN_THREADS, 1) void scan_full_kernel(Params p, int n_items) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[ScanSmem<K, SCAN_FULL>::BYTES];
   // with the longest-first order every workgroup of the grid is mapped below; otherwise
@@ -560,15 +640,15 @@ __global__ __launch_bounds__(SCAN_THREADS, 1) void scan_full_kernel(Params p, in
   }
   SegLoc sl;
   if (!locate_segment(p, sigma, sl)) return;
-  scan_body<K, SCAN_FULL>(p, smem, sl, hv, cg, min(4, (p.V - 64 * cg) / BV), sigma);
+  scan_body<K, SCAN_FULL, C16>(p, smem, sl, hv, cg, min(4, (p.V - 64 * cg) / BV), sigma);
 }
 
-template <int K>
+template <int K, bool C16>
 static hipError_t launch_scan_k(const Params& p, hipStream_t s) {
   const int64_t NCG = (p.V + 63) / 64;
   if (p.bbuf != nullptr) {
     const int64_t items = p.max_segs * p.HV * std::max<int64_t>(NCG, K / 64);
-    hipLaunchKernelGGL((scan_state_kernel<K>), dim3((int)((items + 7) / 8 * 8)), dim3(SCAN_STATE_THREADS), 0, s, p,
+    hipLaunchKernelGGL((scan_state_kernel<K, C16>), dim3((int)((items + 7) / 8 * 8)), dim3(SCAN_STATE_THREADS), 0, s, p,
                        (int)items);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -576,13 +656,14 @@ static hipError_t launch_scan_k(const Params& p, hipStream_t s) {
   const int64_t items = p.max_segs * p.HV * NCG;
   // longest-first order: whole rounds of eight units, NCG workgroups each
   const int64_t grid = p.order ? ((int64_t)p.N * p.HV + 7) / 8 * 8 * NCG : (items + 7) / 8 * 8;
-  hipLaunchKernelGGL((scan_full_kernel<K>), dim3((int)grid), dim3(SCAN_THREADS), 0, s, p, (int)items);
+  hipLaunchKernelGGL((scan_full_kernel<K, C16>), dim3((int)grid), dim3(SCAN_THREADS), 0, s, p, (int)items);
   return hipGetLastError();
 }
 
 hipError_t launch_scan(const Params& p, hipStream_t s) {
   if (p.max_segs * p.HV == 0) return hipSuccess;
-  return p.K == 128 ? launch_scan_k<128>(p, s) : launch_scan_k<64>(p, s);
+  if (p.c16) return p.K == 128 ? launch_scan_k<128, true>(p, s) : launch_scan_k<64, true>(p, s);
+  return p.K == 128 ? launch_scan_k<128, false>(p, s) : launch_scan_k<64, false>(p, s);
 }
 
 }  // namespace kda

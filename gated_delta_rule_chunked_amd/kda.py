@@ -41,7 +41,7 @@ class KdaFwdArgs(ctypes.Structure):
         ("workspace", c_void_p), ("workspace_bytes", c_size_t),
         ("stream", c_void_p),
         ("flags", ctypes.c_uint32), ("hc", c_void_p),
-        ("seg_chunks", c_int32),
+        ("seg_chunks", c_int32), ("chunk", c_int32),
     ]
 
 
@@ -131,7 +131,7 @@ def max_chunks(T, N, B=1, varlen=False):
 
 
 def make_args(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, o=None, ht=None,
-              workspace=None, stream=None, flags=0, hc=None, seg_chunks=0) -> KdaFwdArgs:
+              workspace=None, stream=None, flags=0, hc=None, seg_chunks=0, chunk=64) -> KdaFwdArgs:
     """Fill ``kda_fwd_args`` from torch tensors (shapes as in the header).
 
     q, k: [B, T, HQK, K] bf16; v: [B, T, HV, V] bf16; g: [B, T, HV, K] bf16;
@@ -179,6 +179,7 @@ def make_args(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, o=None, ht
     a.flags = int(flags)
     a.hc = _ptr(hc)
     a.seg_chunks = int(seg_chunks)
+    a.chunk = int(chunk)
     return a
 
 
@@ -244,7 +245,7 @@ def num_chunks(T, cu_seqlens=None, B=1):
 
 def kda_fwd(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, output_final_state=True,
             o=None, workspace=None, beta_logits=False, state_dtype=None, output_chunk_states=False,
-            seg_chunks=0, ht=None, hc=None):
+            seg_chunks=0, ht=None, hc=None, chunk=64):
     """Chunked KDA forward on the current stream.
 
     Returns (o, ht or None), or (o, ht or None, hc) with ``output_chunk_states``:
@@ -255,6 +256,7 @@ def kda_fwd(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, output_final
     ``beta_logits``: beta holds logits and the kernel applies the sigmoid.
     ``state_dtype``: torch.float32 (default) or torch.bfloat16 for h0, ht and hc.
     ``seg_chunks``: segment length of the state scan in chunks (0: chosen by the library).
+    ``chunk``: 64 (default) or 16, FlashKDA's chunk length (no chunk states with 16).
     Allocates o, ht, hc and the workspace with torch unless given.
     """
     import torch
@@ -278,7 +280,8 @@ def kda_fwd(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, output_final
         hc = torch.empty((max_chunks(T, N, B, cu_seqlens is not None), HV, K, V), dtype=sdt, device=q.device)
     if not output_chunk_states:
         hc = None
-    args = make_args(q, k, v, g, beta, scale, h0, cu_seqlens, o, ht, flags=flags, hc=hc, seg_chunks=seg_chunks)
+    args = make_args(q, k, v, g, beta, scale, h0, cu_seqlens, o, ht, flags=flags, hc=hc, seg_chunks=seg_chunks,
+                     chunk=chunk)
     if workspace is None:
         workspace = alloc_workspace(args, q.device)
     args.workspace = workspace.data_ptr()

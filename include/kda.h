@@ -47,7 +47,8 @@ extern "C" {
 #define KDA_ERR_TOO_LARGE     -5  /* kda_fwd_no_alloc: the shapes need more scratch than
                                      KDA_NO_ALLOC_MAX_BYTES                                */
 
-/* Chunk length of the chunked form (tokens per chunk). */
+/* Chunk length of the chunked form (tokens per chunk) by default; see
+ * kda_fwd_args.chunk for the 16-token variant. */
 #define KDA_CHUNK 64
 
 /* Option bits of kda_fwd_args.flags (FlashKDA's input and state variants,
@@ -118,6 +119,14 @@ typedef struct kda_fwd_args {
    * the scan's affine dependence on its start state; results do not depend on
    * it beyond rounding.  Must be >= 0. */
   int32_t seg_chunks;
+  /* Chunk length of the chunked form: 64 (0 also means 64) or 16, the chunk length
+   * of FlashKDA's recurrence kernel ("KDA源码剖析之FlashKDA（下）", kernel 2, template
+   * parameter CHUNK = 16).  With 16 the state is updated every 16 tokens and the
+   * intra-chunk terms (Aqk, the UT/WY inverse, w) span 16 tokens; o and ht equal
+   * those of chunk 64 up to rounding.  hc is not available with 16
+   * (KDA_ERR_UNSUPPORTED); the workspace size does not depend on it.  Other values:
+   * KDA_ERR_UNSUPPORTED. */
+  int32_t chunk;
 } kda_fwd_args;
 
 /* Largest workspace kda_fwd_no_alloc can use: the size of the library's static

@@ -48,7 +48,7 @@ def test_struct_layout_matches_header():
     assert a.B.offset == 64 and a.N.offset == 88 and a.o.offset == 96
     assert a.workspace_bytes.offset == 120 and a.stream.offset == 128
     assert a.flags.offset == 136 and a.hc.offset == 144 and a.seg_chunks.offset == 152
-    assert ctypes.sizeof(a) == 160
+    assert a.chunk.offset == 156 and ctypes.sizeof(a) == 160
 
 
 def args(**over):
@@ -164,6 +164,8 @@ INTER = ("kda_fwd", "kda_fwd_inter")     # entry points that read v, o, h0, ht
     (dict(h0=(1 << 20) + 4), K.KDA_ERR_INVALID_ARG, INTER),
     (dict(flags=4), K.KDA_ERR_INVALID_ARG, ALL),              # unknown option bit
     (dict(hc=(1 << 20) + 8), K.KDA_ERR_INVALID_ARG, ALL),     # misaligned per-chunk states
+    (dict(chunk=32), K.KDA_ERR_UNSUPPORTED, ALL),             # chunk length 64 or 16 only
+    (dict(chunk=16, hc=1 << 20, workspace_bytes=1 << 40), K.KDA_ERR_UNSUPPORTED, ALL),   # no chunk states at 16
     (dict(workspace=0), K.KDA_ERR_WORKSPACE, ALL),
     (dict(workspace_bytes=1000), K.KDA_ERR_WORKSPACE, ALL),
     (dict(workspace=(1 << 20) + 128, workspace_bytes=1 << 40), K.KDA_ERR_WORKSPACE, ALL),
