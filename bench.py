@@ -1,26 +1,33 @@
 """Benchmark of the KDA chunked forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-s S]
-                    [--no-cpu-baseline] [--config N] [--seg-chunks L]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N] [--seg-chunks L]
+                    [--no-cpu-baseline] [--no-variants] [--no-bwd]
+    python bench.py --write-traffic WORKLOAD FETCH_CSV WRITE_CSV [--stats-csv CSV] [--counters-csv CSV ...]
 
 Workload: the 8192-token prefill, B=1, T=8192, H=32 (q/k and value heads),
-K=V=128, chunk 64, bf16 I/O, h0 = 0, seeded synthetic inputs (synth/).
-A step is one call of the whole hot path (intra-chunk kernel, then the
-inter-chunk state scan) on inputs already resident in HBM.  Prints one JSON line.
+K=V=128, chunk 64, bf16 I/O, h0 = 0, seeded synthetic inputs (synth/).  A step is
+one kda_fwd call (the whole hot path: the intra-chunk kernel, then the state scan's
+kernels) on inputs already resident in HBM.  Prints one JSON line.
 
-Timing: W warmup steps, continued for at least --settle-s seconds so that the GPU
-clocks have ramped up; then K steps between two device synchronizations on the
-wall clock (ms_per_step, value).  Inside the same region every fourth step
-(--event-every) records HIP events around each of its two calls, created with
-hipEventDisableSystemFence; they give the per-kernel durations for the roofline
-without the system-scope cache flush a default event record costs.  Each record
-still costs a few microseconds of device time, hence the sampling.
+Timing.  W warmup steps, continued for at least --settle-s seconds so that the GPU
+clocks have ramped up.  The headline (value, ms_per_step) is cold-cache: each of
+the K timed steps follows a 1 GiB read through the caches, which evicts the 4 MB
+L2s and the 256 MB MALL, and is timed alone by two HIP events on the call's stream
+(created with hipEventDisableSystemFence, so recording one costs no system-scope
+cache flush).  The whole timed region, flushes included, sits between two device
+synchronizations.  The warm rate (back-to-back steps, wall clock) and the split
+into the intra call and the scan call (events around every fourth warm step) are
+reported as well.
 
 Algorithmic bytes per token and value head (K = V = 128): q, k, g, v, o at 256 B
-each plus beta 2 B = 1,282 B (q, k per q/k head), plus the final state ht once per
-(sequence, head).  The intra kernel necessarily reads q, k, g, beta (770 B); the
-inter kernel reads v and writes o (512 B) and ht.  Algorithmic flops per token
-and head: 180,224 (dense 64-row tiles).
+each plus beta 2 B = 1,282 B (q, k per q/k head), plus h0 read and ht written once
+per (sequence, head).  The intra kernel necessarily reads q, k, g, beta (770 B); the
+scan reads v and writes o (512 B) and ht.  Algorithmic flops per token and head:
+180,224 (dense 64-row tiles).  `roofline` is the whole call: algorithmic bytes over
+the cold call time, against the HBM peak; `traffic` is the call's HBM bytes from
+the committed rocprofv3 FETCH_SIZE / WRITE_SIZE counters (profiles/), null once a
+kernel's source has changed since they were taken.  `kernels` lists each kernel of
+the call with its necessary bytes, counter bytes and rocprofv3 average duration.
 
 The backward's reverse state scan (kda_bwd_dhu) is timed on the same shape as a
 separate object (``bwd_dhu``), in the checkpoint format of the bwd_dhu page (bf16
@@ -30,6 +37,12 @@ decay row (K fp32) read and the checkpoint (K x V bf16) written; dht read and dh
 written once per (sequence, head).  Its inputs are synthetic stand-ins with the
 forward operands' shapes and magnitudes, built on the device outside the timed
 region (the scan's time does not depend on the values).
+
+--write-traffic turns the CSV output of two rocprofv3 --pmc runs (FETCH_SIZE, then
+WRITE_SIZE) of this script into profiles/traffic_counters.json for WORKLOAD, scaled
+by what the counters read for the 256 MiB device copy the script makes; with
+--stats-csv also the per-kernel average durations of a --kernel-trace --stats run,
+with --counters-csv the per-kernel medians of further counter runs (SQ counters).
 """
 from __future__ import annotations
 
@@ -54,15 +67,19 @@ FLOPS_PER_TOKEN_HEAD = 180224
 # kernels include the host header that chooses between them (a figure taken on one
 # scan must not be reported for a call that now runs the other).
 _CS = "gated_delta_rule_chunked_amd/csrc/"
+_SCAN = [_CS + "kda_scan.hip", _CS + "kda_device.hpp", _CS + "kda_plan.hpp"]
 KERNEL_SOURCES = {
+    "prep": [_CS + "kda_intra.hip"],
+    "chunk_table": [_CS + "kda_intra.hip"],
     "intra": [_CS + "kda_intra.hip", _CS + "kda_device.hpp"],
     "inter": [_CS + "kda_inter.hip", _CS + "kda_device.hpp", _CS + "kda_plan.hpp"],
     "bwd_dhu": [_CS + "kda_bwd.hip", _CS + "kda_device.hpp"],
-    "scan_state": [_CS + "kda_scan.hip", _CS + "kda_device.hpp", _CS + "kda_plan.hpp"],
-    "scan_full": [_CS + "kda_scan.hip", _CS + "kda_device.hpp", _CS + "kda_plan.hpp"],
+    "scan_state": _SCAN,
+    "scan_full": _SCAN,
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hip_runtime_api.h
+CALIB_BYTES = 256 << 20       # the device copy whose counters calibrate FETCH_SIZE / WRITE_SIZE
 
 
 class HipEvents:
@@ -132,41 +149,93 @@ def source_sha(kernel):
     return h.hexdigest()[:16]
 
 
-def traffic_for(workload, call):
-    """HBM bytes per call from the committed rocprofv3 counter summary: the sum over
-    the kernels the call launched for this workload ("intra"; the scan call is the
-    serial scan or the segmented scan's passes), or None when the workload is missing
-    or any of its kernels was measured on a different version of its source."""
-    kernels = {"intra": ["intra"], "inter": ["inter", "scan_state", "scan_full"], "bwd_dhu": ["bwd_dhu"]}[call]
+def kernel_key(name):
+    """Short key of a library kernel from its demangled name ("void kda::scan_full_kernel<128,
+    false>(kda::Params, int)" -> "scan_full"; chunk-16 instances get "_c16"), else None."""
+    import re
+    base = name.split("(")[0].replace("void ", "").strip()
+    m = re.match(r"kda::(\w+?)_kernel(?:<\d+(?:, (true|false))?>)?$", base)
+    if not m:
+        return None
+    return m.group(1) + ("_c16" if m.group(2) == "true" else "")
+
+
+def _source_key(key):
+    return key[:-4] if key.endswith("_c16") else key
+
+
+def load_traffic(workload):
     try:
-        w = json.load(open(TRAFFIC_FILE))["workloads"][workload]
+        return json.load(open(TRAFFIC_FILE))["workloads"][workload]
     except (OSError, KeyError, ValueError):
         return None
-    found = [w[k] for k in kernels if k in w]
-    if not found or any(t.get("source_sha") != source_sha(k) for k, t in zip([k for k in kernels if k in w], found)):
+
+
+def kernel_figures(workload, keys):
+    """Committed counter figures of these kernels for the workload: {key: entry or None}.
+    An entry measured on another version of the kernel's source is dropped (None)."""
+    w = load_traffic(workload) or {}
+    out = {}
+    for k in keys:
+        t = w.get(k)
+        out[k] = t if t is not None and t.get("source_sha") == source_sha(_source_key(k)) else None
+    return out
+
+
+def traffic_for(workload, keys):
+    """HBM bytes per call (the sum over the call's kernels), or None when a kernel's
+    figures are missing or stale."""
+    figs = kernel_figures(workload, keys)
+    if any(v is None or "bytes_per_launch" not in v for v in figs.values()):
         return None
-    return sum(t["bytes_per_launch"] for t in found)
+    return sum(v["bytes_per_launch"] for v in figs.values())
 
 
-def cpu_baseline(d, budget_s=12.0):
-    """The fp64 oracle (token recurrence) on a bounded sample: all heads, the
-    first tokens of the sequence, grown until about budget_s of CPU work."""
-    from threadpoolctl import threadpool_limits
-    from oracle import recurrent
-    n = 32
-    with threadpool_limits(limits=1):
-        while True:
-            a = {k: d[k][:, :n] for k in ("q", "k", "v", "g", "beta")}
-            t0 = time.perf_counter()
-            recurrent(**a, scale=d["scale"])
-            dt = time.perf_counter() - t0
-            if dt > budget_s / 4 or n >= d["T"]:
-                break
-            n = min(d["T"], n * 4)
-    tok_heads_per_s = n * d["HV"] / dt
-    return {"value": tok_heads_per_s / d["HV"], "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} tokens x {d['HV']} heads of the workload, fp64 token recurrence "
-                      f"(numpy, 1 thread), {dt:.1f} s; tokens/s of the full {d['HV']}-head layer"}
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(d, budget_s=18.0):
+    """The fp64 oracle as it stands, on bounded samples of the workload (all heads, the
+    first tokens of the sequence): O1, the token recurrence (numpy, one thread), and O2,
+    the chunked form at chunk 64 (numpy and scipy with every host core given to BLAS).
+    Each sample grows until it takes about a third of the budget.  The headline value is
+    the faster of the two, as tokens/s of the whole layer."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import chunked, recurrent
+    host_cores = len(os.sched_getaffinity(0))
+
+    def timed(fn, threads, n0, cap):
+        n = n0
+        with threadpool_limits(limits=threads):
+            while True:
+                a = {k: d[k][:, :n] for k in ("q", "k", "v", "g", "beta")}
+                t0 = time.perf_counter()
+                fn(**a, scale=d["scale"])
+                dt = time.perf_counter() - t0
+                if dt > budget_s / 9 or n >= cap:
+                    return n, dt
+                n = min(cap, n * 3)
+
+    n1, t1 = timed(recurrent, 1, 64, d["T"])
+    n2, t2 = timed(chunked, host_cores, 64, d["T"])
+    blas = [{"api": i.get("internal_api"), "threads": i.get("num_threads")} for i in threadpool_info()]
+    o1 = {"tokens_per_s": n1 / t1, "threads": 1, "tokens": n1, "seconds": t1,
+          "what": "token recurrence (O1), numpy fp64, vectorised over heads, serial over tokens"}
+    o2 = {"tokens_per_s": n2 / t2, "threads": host_cores, "tokens": n2, "seconds": t2,
+          "what": "chunked form at chunk 64 (O2), numpy/scipy fp64, exact per-element gates, BLAS threads = host cores"}
+    best = o1 if o1["tokens_per_s"] >= o2["tokens_per_s"] else o2
+    return {"value": best["tokens_per_s"], "unit": "tokens/s", "cores": best["threads"], "kind": "oracle",
+            "sample": f"first {best['tokens']} tokens x {d['HV']} heads of the workload, {best['what']}, "
+                      f"{best['seconds']:.1f} s; tokens/s of the full {d['HV']}-head layer",
+            "o1": o1, "o2": o2, "host_cores": host_cores, "cpu_model": cpu_model(), "blas": blas}
 
 
 def bwd_algorithmic_bytes(B, T, HV, K, V, N, C):
@@ -218,37 +287,137 @@ def bench_bwd(t, d, dev, stream, steps, workload):
     return {"ms": ms, "tokens_per_s": B * T / (ms * 1e-3), "algorithmic_bytes": nbytes,
             "roofline": {"bound": "hbm", "kernel": "bwd_dhu", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                         "traffic": traffic_for(workload, "bwd_dhu")},
+                         "traffic": traffic_for(workload, ["bwd_dhu"])},
             "mfma_frac": flops / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
             "checkpoints": "bf16", "states": "fp32", "data": "synthetic stand-ins for qg, kg, w, g2, do, dv, dht"}
+
+
+def write_traffic(workload, fetch_csv, write_csv, stats_csv=None, counter_csvs=()):
+    """profiles/traffic_counters.json entry for `workload` from rocprofv3 --pmc output
+    (run_counter_collection.csv of a FETCH_SIZE run and of a WRITE_SIZE run of this
+    script): per library kernel the median over its dispatches of each counter (KiB),
+    scaled by the ratio of the 256 MiB copy's bytes to what the counter read for it (the
+    copy dispatch with the largest value); with stats_csv (run_kernel_stats.csv of a
+    --kernel-trace --stats run) also each kernel's average duration; with counter_csvs
+    (further --pmc runs) each kernel's median per dispatch of every counter in them,
+    summed over the counter's instances."""
+    import collections
+    import csv
+    import statistics
+
+    def per_dispatch(path):
+        val, name = collections.defaultdict(float), {}
+        for r in csv.DictReader(open(path)):
+            val[r["Dispatch_Id"]] += float(r["Counter_Value"])
+            name[r["Dispatch_Id"]] = r["Kernel_Name"]
+        return val, name
+
+    f, fn = per_dispatch(fetch_csv)
+    w, wn = per_dispatch(write_csv)
+    cf = max(v for k, v in f.items() if "copyBuffer" in fn[k])
+    cw = max(v for k, v in w.items() if "copyBuffer" in wn[k])
+    ff, wf = CALIB_BYTES / (cf * 1024), CALIB_BYTES / (cw * 1024)
+    ent = {"calibration": {"copy_bytes": CALIB_BYTES, "copy_fetch_kib": cf, "copy_write_kib": cw,
+                           "fetch_factor": ff, "write_factor": wf}}
+    acc = collections.defaultdict(lambda: [[], []])
+    for k, v in f.items():
+        key = kernel_key(fn[k])
+        if key:
+            acc[key][0].append(v)
+    for k, v in w.items():
+        key = kernel_key(wn[k])
+        if key:
+            acc[key][1].append(v)
+    for key, (fv, wv) in acc.items():
+        if not fv or not wv:
+            continue
+        fk, wk = statistics.median(fv), statistics.median(wv)
+        ent[key] = {"source_sha": source_sha(_source_key(key)), "fetch_kib": fk, "write_kib": wk,
+                    "fetch_bytes": fk * 1024 * ff, "write_bytes": wk * 1024 * wf,
+                    "bytes_per_launch": fk * 1024 * ff + wk * 1024 * wf}
+    for path in counter_csvs:
+        per = collections.defaultdict(lambda: collections.defaultdict(float))
+        names = {}
+        for r in csv.DictReader(open(path)):
+            per[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+            names[r["Dispatch_Id"]] = r["Kernel_Name"]
+        vals = collections.defaultdict(lambda: collections.defaultdict(list))
+        for did, cs in per.items():
+            key = kernel_key(names[did])
+            if key:
+                for c, v in cs.items():
+                    vals[key][c].append(v)
+        for key, cs in vals.items():
+            ent.setdefault(key, {"source_sha": source_sha(_source_key(key))})
+            ent[key].setdefault("counters", {}).update({c: statistics.median(v) for c, v in cs.items()})
+    if stats_csv:
+        for r in csv.DictReader(open(stats_csv)):
+            key = kernel_key(r["Name"])
+            if key:
+                ent.setdefault(key, {"source_sha": source_sha(_source_key(key))})
+                ent[key]["rocprof_calls"] = int(r["Calls"])
+                ent[key]["rocprof_avg_us"] = float(r["AverageNs"]) / 1e3
+    try:
+        out = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        out = {"workloads": {}}
+    out["note"] = ("HBM bytes per launch: FETCH_SIZE x fetch_factor + WRITE_SIZE x write_factor (KiB), factors "
+                   "from a 256 MiB device copy in the same run; medians over launches; rocprof_avg_us from "
+                   "rocprofv3 --kernel-trace --stats of the default bench command")
+    out["workloads"][workload] = ent
+    json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps(ent, indent=1))
+
+
+def call_kernels(plan, nt, varlen, c16=False):
+    """Keys of the kernels one kda_fwd call launches: the chunk table (varlen) or the
+    counter reset, the intra kernel, then the serial scan, or the segmented scan's
+    passes (the state pass only when a sequence can have several segments: segment
+    length `plan` below the chunk count `nt` of the longest possible sequence)."""
+    sfx = "_c16" if c16 else ""
+    keys = ["chunk_table" if varlen else "prep", "intra" + sfx]
+    if plan == 0:
+        keys.append("inter")
+    else:
+        if plan < nt:   # some sequence has several segments
+            keys.append("scan_state" + sfx)
+        keys.append("scan_full" + sfx)
+    return keys
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=50, help="timed cold-cache steps (the headline)")
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warm-steps", type=int, default=100, help="back-to-back steps for the warm rate")
     ap.add_argument("--event-every", type=int, default=4,
-                    help="time the two calls of every n-th timed step with events (each record costs ~2.5 us)")
+                    help="time the two calls of every n-th warm step with events (each record costs ~2.5 us)")
     ap.add_argument("--settle-s", type=float, default=1.0,
                     help="keep warming up until this many seconds have passed (GPU clocks ramp up under load)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true", help="skip timing the forward's options")
-    ap.add_argument("--cold", type=int, default=20, help="extra cold-cache steps (flush between)")
     ap.add_argument("--no-bwd", action="store_true", help="skip timing the backward state scan")
     ap.add_argument("--config", type=int, default=CFG_ID, choices=sorted(range(1, 6)),
                     help="workload (synth/inputs.py CONFIGS); the headline metric is quoted on 3")
     ap.add_argument("--seg-chunks", type=int, default=0,
                     help="segment length of the state scan (0: the library's choice)")
+    ap.add_argument("--chunk", type=int, default=64, choices=(16, 64), help="chunk length of the timed call")
+    ap.add_argument("--write-traffic", nargs=3, metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--stats-csv", default=None)
+    ap.add_argument("--counters-csv", nargs="*", default=[])
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic, stats_csv=args.stats_csv, counter_csvs=args.counters_csv)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
 
     import torch
-    from gated_delta_rule_chunked_amd import (alloc_workspace, kda_fwd_inter, kda_fwd_intra, kda_fwd_scan_plan,
-                                              load_library, make_args)
+    from gated_delta_rule_chunked_amd import (alloc_workspace, kda_fwd_inter, kda_fwd_intra, kda_fwd_raw,
+                                              kda_fwd_scan_plan, load_library, make_args, max_chunks)
     from synth import make_config_inputs
     from synth.inputs import CONFIGS
 
@@ -263,32 +432,19 @@ def main():
     ht = torch.empty((N, HV, K, V), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     a = make_args(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], h0, cu, o, ht,
-                  stream=stream.cuda_stream, seg_chunks=args.seg_chunks)
+                  stream=stream.cuda_stream, seg_chunks=args.seg_chunks, chunk=args.chunk)
     ws = alloc_workspace(a, dev)
     a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
     plan = kda_fwd_scan_plan(a)   # 0: 16-column serial scan; else 64-column segments of `plan` chunks
+    nt = (T + 63) // 64
 
     # plain copy of known size: the byte-counter calibration kernel for rocprofv3 --pmc
-    calib_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    calib_src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
     calib_dst = torch.empty_like(calib_src)
     calib_dst.copy_(calib_src)
 
-    # Every --event-every-th step of the timed region is bracketed by events: 3j before
-    # its intra call, 3j+1 before its inter call, 3j+2 after it.
-    sampled = list(range(0, args.steps, max(1, args.event_every)))
-    ev = HipEvents(3 * len(sampled))
-    slot = {i: j for j, i in enumerate(sampled)}
-
-    def step(i=None):
-        j = slot.get(i)
-        if j is not None:
-            ev.record(3 * j, stream)
-        kda_fwd_intra(a)
-        if j is not None:
-            ev.record(3 * j + 1, stream)
-        kda_fwd_inter(a)
-        if j is not None:
-            ev.record(3 * j + 2, stream)
+    def step():
+        kda_fwd_raw(a)
 
     # W warmup steps, continued until the clocks have settled (--settle-s of steps)
     t0 = time.perf_counter()
@@ -300,91 +456,118 @@ def main():
             torch.cuda.synchronize()
     torch.cuda.synchronize()
 
+    # ---- headline: K cold-cache steps.  A 1 GiB buffer is read through the caches
+    # before each (evicting L2 and MALL; read, not written, so that no dirty lines are
+    # left whose write-back the step would pay), then the step alone is timed by events.
+    flush = torch.ones(1 << 27, dtype=torch.int64, device=dev)
+    cev = HipEvents(2 * args.steps)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        flush.sum()
+        cev.record(2 * i, stream)
+        step()
+        cev.record(2 * i + 1, stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    region_wall = time.perf_counter() - t0
+    cold = np.array([cev.ms(2 * i, 2 * i + 1) for i in range(args.steps)])
+    del flush
+    ms_per_step = float(cold.mean())
+
+    # ---- warm: back-to-back steps (wall clock); every --event-every-th step is run as its
+    # two calls with events before the intra call, before the scan call and after it
+    t_end = time.perf_counter() + 0.3   # clocks settle again after the cold-cache steps
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+    sampled = list(range(0, args.warm_steps, max(1, args.event_every)))
+    ev = HipEvents(3 * len(sampled))
+    slot = {i: j for j, i in enumerate(sampled)}
+    t0 = time.perf_counter()
+    for i in range(args.warm_steps):
+        j = slot.get(i)
+        if j is None:
+            step()
+            continue
+        ev.record(3 * j, stream)
+        kda_fwd_intra(a)
+        ev.record(3 * j + 1, stream)
+        kda_fwd_inter(a)
+        ev.record(3 * j + 2, stream)
+    torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - t0) * 1e3 / args.warm_steps
     intra_ms = np.array([ev.ms(3 * j, 3 * j + 1) for j in range(len(sampled))])
     inter_ms = np.array([ev.ms(3 * j + 1, 3 * j + 2) for j in range(len(sampled))])
-    ms_per_step = wall * 1e3 / args.steps
 
     # the box's device-copy bandwidth (bytes read + written per second), for context
-    cev = HipEvents(2)
-    cev.record(0, stream)
+    cpy = HipEvents(2)
+    cpy.record(0, stream)
     for _ in range(5):
         calib_dst.copy_(calib_src)
-    cev.record(1, stream)
+    cpy.record(1, stream)
     torch.cuda.synchronize()
-    copy_gbs = 5 * 2 * calib_src.numel() / (cev.ms(0, 1) * 1e-3) / 1e9
+    copy_gbs = 5 * 2 * calib_src.numel() / (cpy.ms(0, 1) * 1e-3) / 1e9
 
-    # cold-cache steps: a 1 GiB buffer read between steps evicts L2 and MALL.  It is
-    # read, not written: a write would leave the caches full of dirty lines whose
-    # write-back the timed step would then pay.
-    cold_ms = None
-    if args.cold:
-        flush = torch.ones(1 << 27, dtype=torch.int64, device=dev)
-        cold = []
-        cev = HipEvents(2)
-        for _ in range(args.cold):
-            flush.sum()
-            cev.record(0, stream)
-            step()
-            cev.record(1, stream)
-            torch.cuda.synchronize()
-            cold.append(cev.ms(0, 1))
-        cold_ms = float(np.median(cold))
-        del flush
-
-    # the forward's options, same workload (informational; not the headline)
+    # the forward's options, same workload, warm back-to-back calls (informational)
     variants_ms = None
     if not args.no_variants:
-        from gated_delta_rule_chunked_amd import KDA_FLAG_BETA_LOGITS, KDA_FLAG_STATE_BF16, num_chunks
+        from gated_delta_rule_chunked_amd import KDA_FLAG_BETA_LOGITS, KDA_FLAG_STATE_BF16
         variants_ms = {}
         ht_bf = torch.empty((N, HV, K, V), dtype=torch.bfloat16, device=dev)
-        hc = torch.empty((num_chunks(T, cu, B), HV, K, V), dtype=torch.float32, device=dev)
+        hc = torch.empty((max_chunks(T, N, B, cu is not None), HV, K, V), dtype=torch.float32, device=dev)
         # the plain call first, timed the same way, as the control for the options
         for name, kw in (("plain", dict(flags=0, ht=ht)),
                          ("beta_logits", dict(flags=KDA_FLAG_BETA_LOGITS, ht=ht)),
                          ("bf16_state", dict(flags=KDA_FLAG_STATE_BF16, ht=ht_bf)),
-                         ("chunk_states_fp32", dict(flags=0, ht=ht, hc=hc))):
+                         ("chunk_states_fp32", dict(flags=0, ht=ht, hc=hc)),
+                         ("chunk16", dict(flags=0, ht=ht, chunk=16))):
             ht_v = kw.pop("ht")
             h0v = None if h0 is None else h0.to(ht_v.dtype)
             av = make_args(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], h0v, cu, o, ht_v,
                            stream=stream.cuda_stream, seg_chunks=args.seg_chunks, **kw)
             av.workspace, av.workspace_bytes = ws.data_ptr(), ws.numel()
-            t_end = time.perf_counter() + 0.3   # clocks settle again after the cold-cache steps
+            t_end = time.perf_counter() + 0.3
             while time.perf_counter() < t_end:
                 for _ in range(20):
-                    kda_fwd_intra(av)
-                    kda_fwd_inter(av)
+                    kda_fwd_raw(av)
                 torch.cuda.synchronize()
             vev = HipEvents(2)
             vev.record(0, stream)
             for _ in range(20):
-                kda_fwd_intra(av)
-                kda_fwd_inter(av)
+                kda_fwd_raw(av)
             vev.record(1, stream)
             torch.cuda.synchronize()
             variants_ms[name] = vev.ms(0, 1) / 20
         del hc, ht_bf
 
     # the backward's stand-in operands are built for fixed-length, whole-chunk sequences
+    workload = CONFIGS[args.config].name + (f"_seg{args.seg_chunks}" if args.seg_chunks else "") + \
+        ("_chunk16" if args.chunk == 16 else "")
     bwd = None
     if not args.no_bwd and d["cu_seqlens"] is None and d["T"] % 64 == 0:
-        bwd = bench_bwd(t, d, dev, stream, args.steps, CONFIGS[args.config].name)
+        bwd = bench_bwd(t, d, dev, stream, args.steps, workload)
 
     tokens = B * T
     value = tokens / (ms_per_step * 1e-3)
-    ab_intra, ab_inter = algorithmic_bytes(d)
-    kern = {"intra": (float(intra_ms.mean()), ab_intra), "inter": (float(inter_ms.mean()), ab_inter)}
-    dom = max(kern, key=lambda k: kern[k][0])
-    dom_ms, dom_bytes = kern[dom]
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    workload = CONFIGS[args.config].name + (f"_seg{args.seg_chunks}" if args.seg_chunks else "")
-    traffic = traffic_for(workload, dom)
-    path_bytes = ab_intra + ab_inter
+    ab_intra, ab_scan = algorithmic_bytes(d)
+    path_bytes = ab_intra + ab_scan
     flops = FLOPS_PER_TOKEN_HEAD * tokens * HV
+    keys = call_kernels(plan, nt, cu is not None, args.chunk == 16)
+    figs = kernel_figures(workload, keys)
+    traffic = traffic_for(workload, keys)
+    achieved = path_bytes / (ms_per_step * 1e-3) / 1e9
+    necessary = {"intra": ab_intra, "inter": ab_scan, "scan_full": ab_scan}
+    kernels = []
+    for k in keys:
+        f = figs[k] or {}
+        kernels.append({"kernel": k, "necessary_bytes": necessary.get(_source_key(k), 0),
+                        "counter_bytes": f.get("bytes_per_launch"), "rocprof_avg_us": f.get("rocprof_avg_us")})
+    calls = {}
+    for name, arr, nb in (("intra", intra_ms, ab_intra), ("scan", inter_ms, ab_scan)):
+        m = float(arr.mean())
+        calls[name] = {"ms": m, "necessary_bytes": nb, "achieved_GBs": nb / (m * 1e-3) / 1e9,
+                       "frac_of_hbm_peak": nb / (m * 1e-3) / (HBM_PEAK_GBS * 1e9)}
     result = {
         "metric": METRIC,
         "value": value,
@@ -393,7 +576,6 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "warmup_steps_run": n_warm,
-        "event_timed_steps": len(sampled),
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -401,19 +583,25 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": CONFIGS[args.config].name, "B": B, "T": T, "N": d["N"], "HQK": d["HQK"], "HV": HV,
-                   "K": K, "V": V, "chunk": 64, "h0": "zero" if d["h0"] is None else "0.1 N(0,1)",
+                   "K": K, "V": V, "chunk": args.chunk, "h0": "zero" if d["h0"] is None else "0.1 N(0,1)",
                    "varlen": d["cu_seqlens"] is not None, "seg_chunks": args.seg_chunks,
                    "scan": "16-column serial" if plan == 0 else f"64-column, segments of {plan} chunks"},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
-        "kernels_ms": {"intra": kern["intra"][0], "inter": kern["inter"][0]},
-        "step_ms_p10_p50_p90": [float(x) for x in np.percentile(intra_ms + inter_ms, [10, 50, 90])],
-        "device_copy_GBs": copy_gbs,
-        "path_roofline": {"algorithmic_bytes": path_bytes,
+        "timing": "cold cache: each timed step follows a 1 GiB read through L2 and MALL and is timed alone "
+                  "with HIP events; ms_per_step is their mean",
+        "step_ms_p10_p50_p90": [float(x) for x in np.percentile(cold, [10, 50, 90])],
+        "timed_region_wall_ms": region_wall * 1e3,
+        "roofline": {"bound": "hbm", "kernel": "kda_fwd call (" + ", ".join(keys) + ")", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": path_bytes},
+        "kernels": kernels,
+        "calls_warm": calls,
+        "warm": {"ms_per_step": warm_ms, "tokens_per_s": tokens / (warm_ms * 1e-3),
+                 "hbm_frac": path_bytes / (warm_ms * 1e-3) / (HBM_PEAK_GBS * 1e9)},
+        "path_roofline": {"algorithmic_bytes": path_bytes, "algorithmic_flops": flops,
                           "hbm_frac": path_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
                           "mfma_frac": flops / (ms_per_step * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12)},
-        "cold_cache_ms_per_step": cold_ms,
-        "options_ms_per_step": variants_ms,
+        "device_copy_GBs": copy_gbs,
+        "options_ms_per_step_warm": variants_ms,
         "bwd_dhu": bwd,
     }
     if not args.no_cpu_baseline:
