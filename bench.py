@@ -245,7 +245,7 @@ def bwd_algorithmic_bytes(B, T, HV, K, V, N, C):
             + 2 * N * HV * K * V * 4)               # dht, dh0
 
 
-def bench_bwd(t, d, dev, stream, steps, workload):
+def bench_bwd(t, d, dev, stream, steps, workload, seg_chunks=0):
     """Time kda_bwd_dhu at the workload's shape; returns the bwd_dhu object."""
     import torch
     from gated_delta_rule_chunked_amd import KDA_FLAG_CKPT_BF16, kda_bwd_dhu_raw, make_bwd_args, num_chunks
@@ -270,7 +270,10 @@ def bench_bwd(t, d, dev, stream, steps, workload):
     dh0 = torch.empty((N, HV, K, V), dtype=torch.float32, device=dev)
     dhc = torch.empty((C, HV, K, V), dtype=torch.bfloat16, device=dev)
     a = make_bwd_args(qg, kg, w, g2, do, dv, dht, d["scale"], None, dv2, dh0, dhc, stream=stream.cuda_stream,
-                      flags=KDA_FLAG_CKPT_BF16)
+                      flags=KDA_FLAG_CKPT_BF16, seg_chunks=seg_chunks)
+    from gated_delta_rule_chunked_amd import kda_bwd_dhu_workspace_bytes
+    ws = torch.empty(max(kda_bwd_dhu_workspace_bytes(a), 256), dtype=torch.uint8, device=dev)
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
     for _ in range(3):
         kda_bwd_dhu_raw(a)
     torch.cuda.synchronize()

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
 ARCH = "gfx950"
-SOURCES = ["kda_api.cpp", "kda_intra.hip", "kda_inter.hip", "kda_scan.hip", "kda_bwd.hip"]
+SOURCES = ["kda_api.cpp", "kda_intra.hip", "kda_inter.hip", "kda_scan.hip", "kda_bwd.hip", "kda_bwd_scan.hip"]
 
 # Packed fp32 VALU ops are disabled on purpose (see the design notes); the host
 # pass prints a harmless "not a recognized feature" warning for it.

@@ -22,7 +22,8 @@ static_assert(offsetof(kda_fwd_args, scale) == 40 && offsetof(kda_fwd_args, B) =
               "argument struct layout (mirrored by the Python binding)");
 static_assert(offsetof(kda_bwd_dhu_args, scale) == 56 && offsetof(kda_bwd_dhu_args, B) == 72 &&
                   offsetof(kda_bwd_dhu_args, dv2) == 96 && offsetof(kda_bwd_dhu_args, stream) == 136 &&
-                  offsetof(kda_bwd_dhu_args, flags) == 144 && sizeof(kda_bwd_dhu_args) == 152,
+                  offsetof(kda_bwd_dhu_args, flags) == 144 && offsetof(kda_bwd_dhu_args, seg_chunks) == 148 &&
+                  sizeof(kda_bwd_dhu_args) == 152,
               "backward argument struct layout (mirrored by the Python binding)");
 static_assert(kda::FLAG_BETA_LOGITS == KDA_FLAG_BETA_LOGITS && kda::FLAG_STATE_BF16 == KDA_FLAG_STATE_BF16 &&
                   kda::FLAG_CKPT_BF16 == KDA_FLAG_CKPT_BF16,
@@ -187,12 +188,24 @@ int hip_status(hipError_t e) {
   return KDA_ERR_HIP;
 }
 
-// Shape checks of the backward scan; the workspace holds only the varlen chunk table.
-int check_bwd_shapes(const kda_bwd_dhu_args* a, int64_t* ws_bytes) {
+// Workspace layout of the backward scan: [varlen: chunk table (N + 2 int32), segment table
+// (N + 1, segmented scan), longest-first order (N, when each sequence is one scan unit and
+// N <= ORDER_MAX_N) | pad to 256 | b | M] (b and M only when a sequence has several segments).
+struct BwdLayout {
+  bool seg_path;
+  int seg_L, seg_S;
+  int64_t max_segs;
+  int64_t segtab_off, order_off;   // byte offsets, or -1
+  int64_t b_off, m_off, total;
+};
+
+// Shape checks of the backward scan and its plan (the forward's rule, kda_plan.hpp).
+int check_bwd_shapes(const kda_bwd_dhu_args* a, BwdLayout* L) {
   if (!a) return KDA_ERR_INVALID_ARG;
   if (a->K != 64 && a->K != 128) return KDA_ERR_UNSUPPORTED;
   if (a->V <= 0 || a->V % kda::BV != 0) return KDA_ERR_UNSUPPORTED;
   if (a->B < 1 || a->T < 0 || a->HV < 1 || a->N < 1) return KDA_ERR_INVALID_ARG;
+  if (a->seg_chunks < 0) return KDA_ERR_INVALID_ARG;
   if (a->cu_seqlens) {
     if (a->B != 1) return KDA_ERR_INVALID_ARG;
   } else if (a->N != a->B) {
@@ -204,10 +217,44 @@ int check_bwd_shapes(const kda_bwd_dhu_args* a, int64_t* ws_bytes) {
   if (max_chunks * a->HV >= ((int64_t)1 << 31) - 8) return KDA_ERR_INVALID_ARG;
   if ((int64_t)a->N * a->HV * (a->V / kda::BV) >= ((int64_t)1 << 31) - 8) return KDA_ERR_INVALID_ARG;
   if (a->N >= (1 << 30)) return KDA_ERR_INVALID_ARG;
-  // varlen: the chunk table (N + 2 int32) and, up to ORDER_MAX_N sequences, the
-  // longest-first sequence order (N int32)
-  const int64_t order_words = a->N <= kda::ORDER_MAX_N ? a->N : 0;
-  *ws_bytes = a->cu_seqlens ? (((int64_t)a->N + 2 + order_words) * 4 + 255) / 256 * 256 : 0;
+  const kda::ScanPlan plan = kda::choose_scan(nt, a->cu_seqlens != nullptr, a->N, a->HV, a->V,
+                                              a->seg_chunks > 0 ? 0 : kda::device_cus(), a->seg_chunks);
+  L->seg_path = plan.seg_path;
+  const int64_t seg_L = std::min<int64_t>(plan.seg_L, std::max<int64_t>(nt, 1));
+  int64_t seg_S = 1, max_segs = 0;
+  bool multi = false;
+  if (plan.seg_path) {
+    if (a->cu_seqlens) {
+      max_segs = (nt + a->N) / seg_L + a->N;
+      multi = seg_L < nt;
+    } else {
+      seg_S = std::max<int64_t>(1, (nt + seg_L - 1) / seg_L);
+      max_segs = (int64_t)a->B * seg_S;
+      multi = seg_S > 1;
+    }
+    if (max_segs * a->HV * ((a->V + 63) / 64 + a->K / 64) >= ((int64_t)1 << 31) - 8) return KDA_ERR_INVALID_ARG;
+  }
+  L->seg_L = (int)seg_L;
+  L->seg_S = (int)seg_S;
+  L->max_segs = max_segs;
+  L->segtab_off = L->order_off = -1;
+  int64_t head = 0;
+  if (a->cu_seqlens) {
+    head = ((int64_t)a->N + 2) * 4;
+    if (plan.seg_path) {
+      L->segtab_off = head;
+      head += ((int64_t)a->N + 1) * 4;
+    }
+    if (!multi && a->N <= kda::ORDER_MAX_N) {
+      L->order_off = head;
+      head += (int64_t)a->N * 4;
+    }
+  }
+  const int64_t bbytes = multi ? max_segs * a->HV * a->K * a->V * 4 : 0;
+  const int64_t mbytes = multi ? max_segs * a->HV * a->K * a->K * 2 : 0;
+  L->b_off = (head + 255) / 256 * 256;
+  L->m_off = L->b_off + bbytes;
+  L->total = (head == 0 && bbytes == 0) ? 0 : L->m_off + mbytes;
   return KDA_OK;
 }
 
@@ -318,17 +365,18 @@ int kda_debug_unpack(const kda_fwd_args* a, void* qg, void* w, void* kg, void* a
 
 int kda_bwd_dhu_workspace_bytes(const kda_bwd_dhu_args* a, size_t* bytes) {
   if (!bytes) return KDA_ERR_INVALID_ARG;
-  int64_t n = 0;
-  int st = check_bwd_shapes(a, &n);
+  BwdLayout L;
+  int st = check_bwd_shapes(a, &L);
   if (st != KDA_OK) return st;
-  *bytes = (size_t)n;
+  *bytes = (size_t)L.total;
   return KDA_OK;
 }
 
 int kda_bwd_dhu(const kda_bwd_dhu_args* a) {
-  int64_t ws = 0;
-  int st = check_bwd_shapes(a, &ws);
+  BwdLayout L;
+  int st = check_bwd_shapes(a, &L);
   if (st != KDA_OK) return st;
+  const int64_t ws = L.total;
   if ((int64_t)a->B * a->T > 0 && (!a->qg || !a->kg || !a->w || !a->g2 || !a->dout || !a->dv2))
     return KDA_ERR_INVALID_ARG;
   const void* a16[] = {a->qg, a->kg, a->w, a->g2, a->dht, a->dh0, a->dhc};
@@ -353,8 +401,16 @@ int kda_bwd_dhu(const kda_bwd_dhu_args* a) {
   p.dv2 = (uint16_t*)a->dv2;
   p.dh0 = a->dh0;
   p.dhc = a->dhc;
-  p.table = a->cu_seqlens ? (int32_t*)a->workspace : nullptr;
-  p.order = (a->cu_seqlens && a->N <= kda::ORDER_MAX_N) ? p.table + a->N + 2 : nullptr;
+  uint8_t* ws8 = (uint8_t*)a->workspace;
+  p.table = a->cu_seqlens ? (int32_t*)ws8 : nullptr;
+  p.segtab = L.segtab_off >= 0 ? (int32_t*)(ws8 + L.segtab_off) : nullptr;
+  p.order = L.order_off >= 0 ? (int32_t*)(ws8 + L.order_off) : nullptr;
+  p.bbuf = L.m_off > L.b_off ? (float*)(ws8 + L.b_off) : nullptr;
+  p.mbuf = L.total > L.m_off ? (uint16_t*)(ws8 + L.m_off) : nullptr;
+  p.seg_path = L.seg_path;
+  p.seg_L = L.seg_L;
+  p.seg_S = L.seg_S;
+  p.max_segs = L.max_segs;
   p.scale = a->scale;
   p.flags = a->flags;
   p.B = a->B; p.T = a->T; p.HV = a->HV; p.K = a->K; p.V = a->V; p.N = a->N;
@@ -362,10 +418,11 @@ int kda_bwd_dhu(const kda_bwd_dhu_args* a) {
   hipStream_t s = (hipStream_t)a->stream;
   if (a->cu_seqlens) {
     const int64_t cap = p.NT + (int64_t)p.N;   // upper bound on the chunk count
-    st = hip_status(kda::launch_chunk_table(p.cu, p.N, p.T, cap, p.table, nullptr, 1, 0, nullptr, nullptr, p.order, s));
+    st = hip_status(kda::launch_chunk_table(p.cu, p.N, p.T, cap, p.table, nullptr, L.seg_path ? L.seg_L : 1,
+                                            L.max_segs, p.segtab, nullptr, p.order, s));
     if (st != KDA_OK) return st;
   }
-  return hip_status(kda::launch_bwd_dhu(p, s));
+  return hip_status(p.seg_path ? kda::launch_bwd_scan(p, s) : kda::launch_bwd_dhu(p, s));
 }
 
 const char* kda_strerror(int status) {

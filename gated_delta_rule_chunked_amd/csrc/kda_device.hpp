@@ -157,6 +157,55 @@ struct SeqLoc {
   int64_t cbase;  // chunk index of the sequence's first chunk
 };
 
+// One segment of one sequence (segmented scans: chunks c0 .. c0 + ncs - 1 of it).
+struct SegLoc {
+  int n, s, nseg;       // sequence, segment within it, its segment count
+  int64_t sigma0;       // index of the sequence's first segment
+  int b;                // batch row
+  int64_t bos;          // first row of the sequence within the batch row
+  int len;              // tokens of the sequence
+  int64_t cbase;        // chunk index of the sequence's first chunk
+  int c0, ncs;          // first chunk of the segment (within the sequence), chunks in it
+};
+
+// Segment sigma -> location.  Returns false when sigma is past the last segment.
+// Works on the forward and the backward parameter blocks (same field names).
+template <class P>
+__device__ __forceinline__ bool locate_segment(const P& p, int64_t sigma, SegLoc& sl) {
+  if (p.cu == nullptr) {
+    const int64_t n = sigma / p.seg_S;
+    if (n >= p.B) return false;
+    sl.n = (int)n;
+    sl.s = (int)(sigma - n * p.seg_S);
+    sl.nseg = p.seg_S;
+    sl.sigma0 = n * p.seg_S;
+    sl.b = (int)n;
+    sl.bos = 0;
+    sl.len = p.T;
+    sl.cbase = n * p.NT;
+  } else {
+    if (sigma >= p.segtab[p.N]) return false;
+    int lo = 0, hi = p.N;                      // segtab[lo] <= sigma < segtab[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.segtab[mid] <= sigma) lo = mid;
+      else hi = mid;
+    }
+    sl.n = lo;
+    sl.sigma0 = p.segtab[lo];
+    sl.s = (int)(sigma - sl.sigma0);
+    sl.nseg = p.segtab[lo + 1] - p.segtab[lo];
+    sl.b = 0;
+    sl.bos = p.cu[lo];
+    sl.len = (int)(p.cu[lo + 1] - p.cu[lo]);
+    sl.cbase = p.table[lo];
+  }
+  const int nc = (sl.len + BT - 1) / BT;
+  sl.c0 = sl.s * p.seg_L;
+  sl.ncs = max(0, min(p.seg_L, nc - sl.c0));
+  return true;
+}
+
 // ds_read_b64_tr_b16, the gfx950 LDS transpose read (8 bytes per lane).  Within
 // each block of 16 lanes, lane 4a + e receives as its element j (a, e, j = 0..3)
 // element e of the 8 bytes addressed by lane 4j + a of the block (lane layout

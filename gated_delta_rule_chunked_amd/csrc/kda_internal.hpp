@@ -61,11 +61,19 @@ struct BwdParams {
   void* dh0;             // state dtype, or nullptr
   void* dhc;             // checkpoint dtype, or nullptr
   int32_t* table;        // varlen chunk table (workspace) or nullptr
-  int32_t* order;        // varlen: sequences longest first (workspace), or nullptr
+  int32_t* order;        // varlen, one scan unit per sequence: sequences longest first, or nullptr
   float scale;
   uint32_t flags;        // FLAG_STATE_BF16, FLAG_CKPT_BF16
   int B, T, HV, K, V, N;
   int NT;                // fixed length: chunks per sequence
+  // Segmented 64-column scan (kda_bwd_scan.hip), the same plan as the forward's
+  bool seg_path;         // the segmented scan runs, else the 16-column serial one (kda_bwd.hip)
+  int seg_L;             // chunks per segment
+  int seg_S;             // fixed length: segments per sequence
+  int64_t max_segs;      // capacity of the segment buffers
+  int32_t* segtab;       // varlen: seg_base[N+1] (workspace), else nullptr
+  float* bbuf;           // K x V fp32 per (segment, HV): the dh a segment hands to the next older one
+  uint16_t* mbuf;        // K x K bf16 per (segment, HV): the segment's transition, as P-order A fragments
 };
 
 // Host launchers (return the hipError_t of the launch).
@@ -84,6 +92,7 @@ hipError_t launch_intra(const Params& p, hipStream_t s);
 hipError_t launch_inter(const Params& p, hipStream_t s);
 hipError_t launch_scan(const Params& p, hipStream_t s);          // segmented scan (both passes)
 hipError_t launch_bwd_dhu(const BwdParams& p, hipStream_t s);
+hipError_t launch_bwd_scan(const BwdParams& p, hipStream_t s);   // segmented scan (both passes)
 hipError_t launch_unpack(const Params& p, uint16_t* qg, uint16_t* w, uint16_t* kg,
                          uint16_t* aqk, uint16_t* tmb, float* alpha, hipStream_t s);
 

@@ -83,53 +83,6 @@ struct ScanSmem {
   static_assert(BYTES <= 160 * 1024, "fits the LDS of one CU");
 };
 
-// One segment of one sequence.
-struct SegLoc {
-  int n, s, nseg;       // sequence, segment within it, its segment count
-  int64_t sigma0;       // index of the sequence's first segment
-  int b;                // batch row
-  int64_t bos;          // first row of the sequence within the batch row
-  int len;              // tokens of the sequence
-  int64_t cbase;        // chunk index of the sequence's first chunk
-  int c0, ncs;          // first chunk of the segment (within the sequence), chunks in it
-};
-
-// Segment sigma -> location.  Returns false when sigma is past the last segment.
-__device__ __forceinline__ bool locate_segment(const Params& p, int64_t sigma, SegLoc& sl) {
-  if (p.cu == nullptr) {
-    const int64_t n = sigma / p.seg_S;
-    if (n >= p.B) return false;
-    sl.n = (int)n;
-    sl.s = (int)(sigma - n * p.seg_S);
-    sl.nseg = p.seg_S;
-    sl.sigma0 = n * p.seg_S;
-    sl.b = (int)n;
-    sl.bos = 0;
-    sl.len = p.T;
-    sl.cbase = n * p.NT;
-  } else {
-    if (sigma >= p.segtab[p.N]) return false;
-    int lo = 0, hi = p.N;                      // segtab[lo] <= sigma < segtab[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.segtab[mid] <= sigma) lo = mid;
-      else hi = mid;
-    }
-    sl.n = lo;
-    sl.sigma0 = p.segtab[lo];
-    sl.s = (int)(sigma - sl.sigma0);
-    sl.nseg = p.segtab[lo + 1] - p.segtab[lo];
-    sl.b = 0;
-    sl.bos = p.cu[lo];
-    sl.len = (int)(p.cu[lo + 1] - p.cu[lo]);
-    sl.cbase = p.table[lo];
-  }
-  const int nc = (sl.len + BT - 1) / BT;
-  sl.c0 = sl.s * p.seg_L;
-  sl.ncs = max(0, min(p.seg_L, nc - sl.c0));
-  return true;
-}
-
 // The chunks of one segment for one value head and 64-column group (`grp`: value
 // columns 64 grp.., or key columns 64 grp.. of M in SCAN_M), with `ntiles` active
 // column waves.  Waves from `lwave0` on are the loader waves; column wave cw is wave

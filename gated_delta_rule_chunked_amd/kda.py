@@ -54,7 +54,7 @@ class KdaBwdDhuArgs(ctypes.Structure):
         ("B", c_int32), ("T", c_int32), ("HV", c_int32), ("K", c_int32), ("V", c_int32), ("N", c_int32),
         ("dv2", c_void_p), ("dh0", c_void_p), ("dhc", c_void_p),
         ("workspace", c_void_p), ("workspace_bytes", c_size_t),
-        ("stream", c_void_p), ("flags", ctypes.c_uint32),
+        ("stream", c_void_p), ("flags", ctypes.c_uint32), ("seg_chunks", c_int32),
     ]
 
 
@@ -298,7 +298,7 @@ def kda_debug_unpack(args: KdaFwdArgs, qg=None, w=None, kg=None, aqk=None, tmb=N
 
 
 def make_bwd_args(qg, kg, w, g2, do, dv=None, dht=None, scale=None, cu_seqlens=None, dv2=None, dh0=None,
-                  dhc=None, workspace=None, stream=None, flags=0) -> KdaBwdDhuArgs:
+                  dhc=None, workspace=None, stream=None, flags=0, seg_chunks=0) -> KdaBwdDhuArgs:
     """Fill ``kda_bwd_dhu_args`` from torch tensors (shapes as in the header).
 
     qg, kg, w: [B, T, HV, K] bf16; g2: [B, T, HV, K] fp32; do, dv, dv2: [B, T, HV, V]
@@ -341,6 +341,7 @@ def make_bwd_args(qg, kg, w, g2, do, dv=None, dht=None, scale=None, cu_seqlens=N
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a.stream = stream
     a.flags = int(flags)
+    a.seg_chunks = int(seg_chunks)
     return a
 
 
@@ -359,7 +360,7 @@ def kda_bwd_dhu_raw(args: KdaBwdDhuArgs) -> None:
 
 
 def kda_bwd_dhu(qg, kg, w, g2, do, dv=None, dht=None, scale=None, cu_seqlens=None, state_dtype=None,
-                checkpoint_dtype=None, output_dh0=True, output_checkpoints=True):
+                checkpoint_dtype=None, output_dh0=True, output_checkpoints=True, seg_chunks=0):
     """Reverse state scan of the chunked backward on the current stream.
 
     Returns (dv2, dhc or None, dh0 or None): dv2 [B, T, HV, V] bf16, dhc [C, HV, K, V]
@@ -386,7 +387,8 @@ def kda_bwd_dhu(qg, kg, w, g2, do, dv=None, dht=None, scale=None, cu_seqlens=Non
     dhc = None
     if output_checkpoints:   # varlen: room for the bound, no look at the lengths on the host
         dhc = torch.empty((max_chunks(T, N, B, cu_seqlens is not None), HV, K, V), dtype=cdt, device=qg.device)
-    args = make_bwd_args(qg, kg, w, g2, do, dv, dht, scale, cu_seqlens, dv2, dh0, dhc, flags=flags)
+    args = make_bwd_args(qg, kg, w, g2, do, dv, dht, scale, cu_seqlens, dv2, dh0, dhc, flags=flags,
+                         seg_chunks=seg_chunks)
     n = kda_bwd_dhu_workspace_bytes(args)
     workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=qg.device)
     args.workspace = workspace.data_ptr()

@@ -242,17 +242,26 @@ typedef struct kda_bwd_dhu_args {
   void* dv2;
   void* dh0;
   void* dhc;
-  /* Scratch (device, 256-byte aligned, size from kda_bwd_dhu_workspace_bytes;
-   * zero bytes, so NULL is allowed, for fixed length; varlen: the chunk table and
-   * the sequences' longest-first order, written by the call itself). */
+  /* Scratch (device, 256-byte aligned, size from kda_bwd_dhu_workspace_bytes: for varlen
+   * the chunk and segment tables and the sequences' longest-first order, and, when a
+   * sequence has several segments, each segment's b (fp32 K x V) and M (bf16 K x K) per
+   * value head; all written by the call itself.  Zero bytes, so NULL is allowed, for
+   * fixed length with one segment per sequence). */
   void* workspace;
   size_t workspace_bytes;
   void* stream;                /* hipStream_t */
   uint32_t flags;              /* KDA_FLAG_STATE_BF16 | KDA_FLAG_CKPT_BF16; others rejected */
+  /* Segment length of the scan in chunks, or 0 to let the library choose (the forward's
+   * rule, kda_fwd_scan_plan).  As in the forward, sequences cut into segments are scanned in
+   * parallel by 64-column workgroups and joined through the recursion's affine dependence on
+   * dh (a state pass computes each segment's hand-on b and transition M first); results do
+   * not depend on it beyond rounding.  Must be >= 0. */
+  int32_t seg_chunks;
 } kda_bwd_dhu_args;
 
-/* Workspace size for these arguments (host only; reads the shape fields and
- * whether cu_seqlens is NULL). */
+/* Workspace size for these arguments (host only; reads the shape fields, whether
+ * cu_seqlens is NULL and seg_chunks; with seg_chunks == 0 the plan follows the current
+ * device's compute-unit count, as for the forward). */
 int kda_bwd_dhu_workspace_bytes(const kda_bwd_dhu_args* a, size_t* bytes);
 
 /* The reverse state scan: dv2, dh0 and dhc from qg, kg, w, g2, dout, dv, dht.

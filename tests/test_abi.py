@@ -191,7 +191,7 @@ def test_bwd_struct_layout_matches_header():
     assert a.g2.offset == 24 and a.dht.offset == 48 and a.scale.offset == 56 and a.cu_seqlens.offset == 64
     assert a.B.offset == 72 and a.N.offset == 92 and a.dv2.offset == 96 and a.dhc.offset == 112
     assert a.workspace_bytes.offset == 128 and a.stream.offset == 136 and a.flags.offset == 144
-    assert ctypes.sizeof(a) == 152
+    assert a.seg_chunks.offset == 148 and ctypes.sizeof(a) == 152
 
 
 def bwd_args(**over):
@@ -212,13 +212,26 @@ def bwd_ws(a):
 
 
 def test_bwd_workspace_bytes(lib):
-    # fixed length needs no scratch; varlen holds the chunk table (N + 2 int32) and the
-    # longest-first sequence order (N int32, up to 2048 sequences)
-    assert bwd_ws(bwd_args(B=1, T=8192, HV=32)) == (0, 0)
-    assert bwd_ws(bwd_args(N=5, cu_seqlens=1 << 20)) == (0, 256)
-    assert bwd_ws(bwd_args(N=70, cu_seqlens=1 << 20)) == (0, 768)
-    assert bwd_ws(bwd_args(N=3000, cu_seqlens=1 << 20)) == (0, (3002 * 4 + 255) // 256 * 256)
+    # The forward's plan (256 compute units when no device is seen).  Fixed length on the
+    # serial scan needs no scratch; the segmented scan adds b (fp32 K x V) and M (bf16 K x K)
+    # per (segment, head) when a sequence has several segments.  Varlen holds the chunk table
+    # (N + 2 int32), with the segmented scan the segment table (N + 1), and the longest-first
+    # sequence order (N, when every sequence is one scan unit, up to 2048 sequences).
+    KV4, KK2 = 128 * 128 * 4, 128 * 128 * 2
+    # 8192 tokens, 32 heads: 4 segments of 32 chunks
+    assert bwd_ws(bwd_args(B=1, T=8192, HV=32)) == (0, 4 * 32 * (KV4 + KK2))
+    assert bwd_ws(bwd_args(B=1, T=8192, HV=32, seg_chunks=128)) == (0, 0)   # one segment: no b, M
+    assert bwd_ws(bwd_args(B=1, T=4096, HV=32)) == (0, 0)                   # the serial scan
+    assert bwd_ws(bwd_args(N=5, cu_seqlens=1 << 20)) == (0, 256)            # serial: 7 + 5 words
+    # 70 sequences: 560 wide workgroups, one segment each: 72 + 71 + 70 words -> 1024
+    assert bwd_ws(bwd_args(N=70, cu_seqlens=1 << 20)) == (0, 1024)
+    # 3000 sequences: no longest-first order past 2048
+    assert bwd_ws(bwd_args(N=3000, cu_seqlens=1 << 20)) == (0, ((3002 + 3001) * 4 + 255) // 256 * 256)
+    # forced segments of 2 chunks on 4 varlen sequences: (4 + 5) // 2 + 5 = 9 segments
+    st, n = bwd_ws(bwd_args(N=5, cu_seqlens=1 << 20, HV=2, seg_chunks=2))
+    assert st == 0 and n == 256 + ((4 + 5) // 2 + 5) * 2 * (KV4 + KK2)
     assert bwd_ws(bwd_args(K=96))[0] == K.KDA_ERR_UNSUPPORTED
+    assert bwd_ws(bwd_args(seg_chunks=-1))[0] == K.KDA_ERR_INVALID_ARG
     assert lib.kda_bwd_dhu_workspace_bytes(None, None) == K.KDA_ERR_INVALID_ARG
 
 
