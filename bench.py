@@ -74,6 +74,8 @@ KERNEL_SOURCES = {
     "intra": [_CS + "kda_intra.hip", _CS + "kda_device.hpp"],
     "inter": [_CS + "kda_inter.hip", _CS + "kda_device.hpp", _CS + "kda_plan.hpp"],
     "bwd_dhu": [_CS + "kda_bwd.hip", _CS + "kda_device.hpp"],
+    "bscan_state": [_CS + "kda_bwd_scan.hip", _CS + "kda_device.hpp", _CS + "kda_plan.hpp"],
+    "bscan_full": [_CS + "kda_bwd_scan.hip", _CS + "kda_device.hpp", _CS + "kda_plan.hpp"],
     "scan_state": _SCAN,
     "scan_full": _SCAN,
 }
@@ -245,8 +247,17 @@ def bwd_algorithmic_bytes(B, T, HV, K, V, N, C):
             + 2 * N * HV * K * V * 4)               # dht, dh0
 
 
-def bench_bwd(t, d, dev, stream, steps, workload, seg_chunks=0):
-    """Time kda_bwd_dhu at the workload's shape; returns the bwd_dhu object."""
+def bwd_kernels(plan, nt):
+    """Keys of the kernels one fixed-length kda_bwd_dhu call launches.  The backward picks its
+    scan with the forward's rule on the same shape: `plan` is kda_fwd_scan_plan at chunk 64."""
+    if plan == 0:
+        return ["bwd_dhu"]
+    return (["bscan_state"] if plan < nt else []) + ["bscan_full"]
+
+
+def bench_bwd(t, d, dev, stream, steps, workload, keys, seg_chunks=0):
+    """Time kda_bwd_dhu at the workload's shape; returns the bwd_dhu object.  `keys` names the
+    kernels one call launches (their summed counter bytes are the object's traffic)."""
     import torch
     from gated_delta_rule_chunked_amd import KDA_FLAG_CKPT_BF16, kda_bwd_dhu_raw, make_bwd_args, num_chunks
     B, T, HV, K, V, N = d["B"], d["T"], d["HV"], d["K"], d["V"], d["N"]
@@ -288,9 +299,10 @@ def bench_bwd(t, d, dev, stream, steps, workload, seg_chunks=0):
     achieved = nbytes / (ms * 1e-3) / 1e9
     flops = 6 * K * V * B * T * HV       # DV, QD, WD per token and head
     return {"ms": ms, "tokens_per_s": B * T / (ms * 1e-3), "algorithmic_bytes": nbytes,
+            "kernels": keys,
             "roofline": {"bound": "hbm", "kernel": "bwd_dhu", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                         "traffic": traffic_for(workload, ["bwd_dhu"])},
+                         "traffic": traffic_for(workload, keys)},
             "mfma_frac": flops / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
             "checkpoints": "bf16", "states": "fp32", "data": "synthetic stand-ins for qg, kg, w, g2, do, dv, dht"}
 
@@ -549,7 +561,10 @@ def main():
         ("_chunk16" if args.chunk == 16 else "")
     bwd = None
     if not args.no_bwd and d["cu_seqlens"] is None and d["T"] % 64 == 0:
-        bwd = bench_bwd(t, d, dev, stream, args.steps, workload)
+        a64 = type(a).from_buffer_copy(a)
+        a64.chunk = 64
+        bwd = bench_bwd(t, d, dev, stream, args.steps, workload, bwd_kernels(kda_fwd_scan_plan(a64), nt),
+                        seg_chunks=args.seg_chunks)
 
     tokens = B * T
     value = tokens / (ms_per_step * 1e-3)
