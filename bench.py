@@ -208,8 +208,9 @@ def cpu_baseline(d, budget_s=18.0):
     """The fp64 oracle as it stands, on bounded samples of the workload (all heads, the
     first tokens of the sequence): O1, the token recurrence (numpy, one thread), and O2,
     the chunked form at chunk 64 (numpy and scipy with every host core given to BLAS).
-    Each sample grows until it takes about a third of the budget.  The headline value is
-    the faster of the two, as tokens/s of the whole layer."""
+    Each sample grows by threes until a run takes a thirtieth of the budget, then jumps to the
+    size that should take a third of it, so the two timed samples take about 12 s together.
+    The headline value is the faster of the two, as tokens/s of the whole layer."""
     from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import chunked, recurrent
     host_cores = len(os.sched_getaffinity(0))
@@ -222,9 +223,10 @@ def cpu_baseline(d, budget_s=18.0):
                 t0 = time.perf_counter()
                 fn(**a, scale=d["scale"])
                 dt = time.perf_counter() - t0
-                if dt > budget_s / 9 or n >= cap:
+                if dt > budget_s / 6 or n >= cap:
                     return n, dt
-                n = min(cap, n * 3)
+                # a run this long predicts the rate well enough to size the timed one
+                n = min(cap, int(n * budget_s / 3 / dt) if dt > budget_s / 30 else n * 3)
 
     n1, t1 = timed(recurrent, 1, 64, d["T"])
     n2, t2 = timed(chunked, host_cores, 64, d["T"])
