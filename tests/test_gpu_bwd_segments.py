@@ -84,3 +84,12 @@ def test_bwd_segments_agree_with_the_serial_scan():
     from _gpu_util import nerr
     for u, v in zip(a, b):
         assert nerr(u, v) <= 5e-3
+
+
+def test_bwd_long_sequence_library_plan():
+    # 513 chunks, 2 value heads, the library's own choice: eight segments of 65 chunks
+    # (the forward's rule), so the oldest segment's prologue hops over six inner segments
+    d = make_inputs(96, B=1, T=64 * 512 + 37, HQK=1, HV=2, K=128, V=128, has_h0=False)
+    gr = make_grads(d, 960)
+    x = scan_inputs(d, gr)
+    check(run_gpu(x, d), reference(x, d), "513 chunks, library plan")

@@ -184,3 +184,21 @@ def test_varlen_order_limit(n_seq):
     eo, eh = nerr(o_np, o_ref), nerr(ht_np, ht_ref)
     print(f"  {n_seq} sequences: o {eo:.2e} ht {eh:.2e}", flush=True)
     assert eo <= TOL and eh <= TOL
+
+
+def test_very_long_sequence_eight_long_segments():
+    # 1,025 chunks, 2 value heads: the library picks eight segments of 129 chunks, so the
+    # last segment's prologue chains seven (M, b) hops and every segment loops 129 times
+    import torch
+    from gated_delta_rule_chunked_amd import kda_fwd_scan_plan, make_args
+    d = make_inputs(137, B=1, T=64 * 1024 + 37, HQK=1, HV=2, K=128, V=128, has_h0=True)
+    t = to_device(d)
+    a = make_args(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], t["h0"], None,
+                  torch.empty_like(t["v"]), None)
+    plan = kda_fwd_scan_plan(a)
+    assert plan == 129, plan
+    o, ht = run(d, t)
+    o_ref, ht_ref = reference(d)
+    eo, eh = nerr(o, o_ref), nerr(ht, ht_ref)
+    print(f"  1025 chunks, plan {plan}: o {eo:.2e} ht {eh:.2e}", flush=True)
+    assert np.all(np.isfinite(o)) and eo <= TOL and eh <= TOL
