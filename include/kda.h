@@ -18,7 +18,11 @@
  * Conventions for every entry point below
  *   - Tensor pointers are DEVICE pointers to contiguous row-major memory; the
  *     caller owns every buffer.  The library never allocates, frees or
- *     synchronises, and keeps no state between calls (thread-safe, reentrant).
+ *     synchronises.  Between calls it keeps only per-device caches (the
+ *     compute-unit count, and the address of kda_fwd_no_alloc's static scratch),
+ *     filled race-free on first use: every entry point is thread-safe and
+ *     reentrant, except that kda_fwd_no_alloc calls overlapping in time on one
+ *     device share that scratch (see there).
  *   - bf16 tensors are IEEE bfloat16 bit patterns (uint16).
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream);
  *     calls return before the GPU work finishes.
@@ -149,8 +153,8 @@ int kda_fwd_workspace_bytes(const kda_fwd_args* a, size_t* bytes);
  * 64-column workgroups than compute units one segment per sequence; else, for
  * sequences of 96 chunks or more (the mean for varlen), 2 to 8 segments so that
  * the full pass fills the device in one round; else the serial scan when its
- * workgroups fill at least half the device or sequences are shorter than 64
- * chunks, and segments of max(8, chunks / 8) otherwise. */
+ * workgroups fill at least half the device or sequences are shorter than 32
+ * chunks, and segments of max(4, ceil(chunks / 8)) otherwise. */
 int kda_fwd_scan_plan(const kda_fwd_args* a, int32_t* seg_chunks);
 
 /* The whole chunked forward: o (and ht) from q, k, v, g, beta, h0 (kernel-fun
