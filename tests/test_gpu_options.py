@@ -78,13 +78,19 @@ def test_chunk_states(case):
     if sdt == torch.bfloat16:
         h0_used = round_to_bf16(d["h0"])
         t["h0"] = torch.from_numpy(h0_used).to(torch.bfloat16).cuda()
-    o, ht, hc = run(d, t, output_chunk_states=True, state_dtype=sdt)
+    # hc starts as zeros: the rows past the written chunks must stay untouched
+    from gated_delta_rule_chunked_amd import max_chunks
+    N = d["B"] if d["cu_seqlens"] is None else len(d["cu_seqlens"]) - 1
+    C = max_chunks(d["T"], N, d["B"], d["cu_seqlens"] is not None)
+    hc0 = torch.zeros((C, d["HV"], d["K"], d["V"]), dtype=sdt, device="cuda")
+    o, ht, hc = run(d, t, output_chunk_states=True, state_dtype=sdt, hc=hc0)
     o_plain, ht_plain = run(d, t, state_dtype=sdt)
     assert np.array_equal(o, o_plain) and np.array_equal(ht, ht_plain)   # hc changes nothing else
     _, _, inter = chunked(**{k: d[k] for k in FIELDS}, scale=d["scale"], h0=h0_used,
                           cu_seqlens=d["cu_seqlens"], chunk=64, return_intermediates=True)
     # varlen: hc has room for ceil(T/64) + N chunks; the first sum ceil(len/64) are written
     assert hc.shape[0] == (len(inter) if case == "fixed" else (d["T"] + 63) // 64 + len(d["cu_seqlens"]) - 1)
+    assert np.all(hc[len(inter):] == 0)
     hc = hc[:len(inter)]
     ref = np.stack([ci["h"] for ci in inter])
     e = nerr(hc, ref)
