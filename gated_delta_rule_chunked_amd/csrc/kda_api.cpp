@@ -126,9 +126,10 @@ int check_shapes(const kda_fwd_args* a, kda::WsLayout* L) {
 
 enum Need { NEED_INTRA = 1, NEED_INTER = 2 };
 
-int check_call(const kda_fwd_args* a, int need, kda::Params* p) {
-  kda::WsLayout L;
-  int st = check_shapes(a, &L);
+// Everything a call needs but its workspace: shapes, tensor pointers and their
+// alignment, options, the scale.
+int check_args(const kda_fwd_args* a, int need, kda::WsLayout* L) {
+  int st = check_shapes(a, L);
   if (st != KDA_OK) return st;
   const bool any_tokens = (int64_t)a->B * a->T > 0;
   if (need & NEED_INTRA) {
@@ -144,11 +145,18 @@ int check_call(const kda_fwd_args* a, int need, kda::Params* p) {
   if (!aligned(a->cu_seqlens, 8) || !aligned(a->hc, 16)) return KDA_ERR_INVALID_ARG;
   if (a->chunk == 16 && a->hc) return KDA_ERR_UNSUPPORTED;
   if (a->flags & ~(uint32_t)(KDA_FLAG_BETA_LOGITS | KDA_FLAG_STATE_BF16)) return KDA_ERR_INVALID_ARG;
+  if (!(a->scale == a->scale)) return KDA_ERR_INVALID_ARG;  // NaN scale
+  return KDA_OK;
+}
+
+int check_call(const kda_fwd_args* a, int need, kda::Params* p) {
+  kda::WsLayout L;
+  int st = check_args(a, need, &L);
+  if (st != KDA_OK) return st;
   if (L.total_bytes > 0) {
     if (!a->workspace || !aligned(a->workspace, 256)) return KDA_ERR_WORKSPACE;
     if (a->workspace_bytes < (size_t)L.total_bytes) return KDA_ERR_WORKSPACE;
   }
-  if (!(a->scale == a->scale)) return KDA_ERR_INVALID_ARG;  // NaN scale
   p->q = (const uint16_t*)a->q;
   p->k = (const uint16_t*)a->k;
   p->v = (const uint16_t*)a->v;
@@ -341,6 +349,9 @@ int kda_fwd_no_alloc(const kda_fwd_args* a) {
   int st = check_shapes(a, &L);
   if (st != KDA_OK) return st;
   if ((uint64_t)L.total_bytes > (uint64_t)KDA_NO_ALLOC_MAX_BYTES) return KDA_ERR_TOO_LARGE;
+  // every argument is checked before the scratch is looked up (a HIP call)
+  st = check_args(a, NEED_INTRA | NEED_INTER, &L);
+  if (st != KDA_OK) return st;
   uint8_t* ws = nullptr;
   st = scratch_on_current_device(&ws);
   if (st != KDA_OK) return st;
