@@ -93,3 +93,19 @@ def test_bwd_long_sequence_library_plan():
     gr = make_grads(d, 960)
     x = scan_inputs(d, gr)
     check(run_gpu(x, d), reference(x, d), "513 chunks, library plan")
+
+
+@pytest.mark.parametrize("n_seq", [300, 2048, 2049])
+def test_bwd_many_sequences_library_plan(n_seq):
+    # many short varlen sequences: the library gives each (sequence, head, 64-column group)
+    # its own workgroup, longest first (the chunk table kernel sorts up to 2,048 sequences
+    # on the device; past that the given order); empty sequences give dh0 = dht exactly
+    rng = np.random.default_rng(970 + n_seq)
+    lengths = [int(x) for x in rng.integers(0, 100 if n_seq == 300 else 4, size=n_seq)]
+    lengths[7] = 0
+    d = make_inputs(97, B=1, T=0, HQK=1, HV=1, K=64, V=64, has_h0=False, lengths=lengths)
+    gr = make_grads(d, 9700 + n_seq)
+    x = scan_inputs(d, gr)
+    got, ref = run_gpu(x, d), reference(x, d)
+    check(got, ref, f"{n_seq} sequences")
+    assert np.array_equal(got[2][7], gr["dht"][7].astype(np.float64))
