@@ -100,3 +100,22 @@ def test_gpu_entry_points_refuse_host_tensors():
     t = fwd_tensors()
     with pytest.raises(RuntimeError, match="GPU only"):
         K.kda_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"])
+
+
+def test_missing_library_fails_loudly():
+    # a fresh process whose library path does not exist: the binding raises, it never
+    # falls back to anything else
+    import subprocess
+    import sys
+    code = ("import gated_delta_rule_chunked_amd.kda as K\n"
+            "try:\n"
+            "    K.load_library('/nonexistent/libkda.so')\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n"
+            "else:\n"
+            "    print('loaded')\n")
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.startswith("raised:") and "missing" in r.stdout
