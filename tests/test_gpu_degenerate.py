@@ -110,3 +110,34 @@ def test_zero_values_from_zero_state(opts):
 def test_single_token_sequences(opts):
     d = make_inputs(806, B=1, T=0, HQK=1, HV=2, K=128, V=64, has_h0=True, lengths=[1, 1, 1, 0, 1])
     run_and_check(d, opts)
+
+
+@pytest.mark.parametrize("opts", OPTS, ids=IDS)
+@pytest.mark.parametrize("has_h0", [True, False])
+def test_fixed_length_without_tokens(opts, has_h0):
+    # B sequences of T = 0 tokens: no o rows, and each final state is its initial state
+    import torch
+    from gated_delta_rule_chunked_amd import kda_fwd
+    d = make_inputs(807, B=2, T=0, HQK=1, HV=2, K=128, V=64, has_h0=has_h0)
+    t = to_device(d)
+    ht = torch.full((2, 2, 128, 64), float("nan"), dtype=torch.float32, device="cuda")
+    o, ht = kda_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=d["scale"], h0=t["h0"], ht=ht, **opts)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 0, 2, 64)
+    want = d["h0"] if has_h0 else np.zeros((2, 2, 128, 64), np.float32)
+    assert np.array_equal(ht.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("seg", [0, 2])
+def test_backward_without_tokens(seg):
+    # T = 0: no dv2 rows, no checkpoints, and dh0 is dht
+    import torch
+    from gated_delta_rule_chunked_amd import kda_bwd_dhu
+    bf = torch.bfloat16
+    e = lambda *s, dt=bf: torch.empty(s, dtype=dt, device="cuda")
+    dht = torch.randn((2, 2, 128, 64), device="cuda")
+    dv2, dhc, dh0 = kda_bwd_dhu(e(2, 0, 2, 128), e(2, 0, 2, 128), e(2, 0, 2, 128), e(2, 0, 2, 128, dt=torch.float32),
+                                e(2, 0, 2, 64), e(2, 0, 2, 64), dht, scale=0.1, seg_chunks=seg)
+    torch.cuda.synchronize()
+    assert dv2.shape == (2, 0, 2, 64) and dhc.shape[0] == 0
+    assert torch.equal(dh0, dht)
