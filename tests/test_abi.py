@@ -268,3 +268,20 @@ def test_no_alloc_rejects_shapes_beyond_its_static_buffer(lib):
     assert lib.kda_fwd_no_alloc(ctypes.byref(a)) == K.KDA_ERR_TOO_LARGE
     assert "KDA_NO_ALLOC_MAX_BYTES" in K.kda_strerror(K.KDA_ERR_TOO_LARGE)
     assert lib.kda_fwd_no_alloc(None) == K.KDA_ERR_INVALID_ARG
+
+
+def test_shape_limits(lib):
+    # the largest shapes the kernels' 32-bit grid and record indices take, and one past them
+    limit = (1 << 31) - 8                                     # (chunk, value head) records
+    hv = 1 << 20
+    st, n = ws(args(B=1, T=64 * 2047, HQK=1, HV=hv, N=1))     # 2047 * 2^20 records: inside
+    assert st == 0 and n >= 2047 * hv * 61952 and 2047 * hv < limit
+    assert ws(args(B=1, T=64 * 2048, HQK=1, HV=hv, N=1))[0] == K.KDA_ERR_INVALID_ARG   # 2^31 records
+    assert ws(args(B=1 << 20, T=1 << 21, HQK=1, HV=1, N=1 << 20))[0] == K.KDA_ERR_INVALID_ARG  # 2^41 rows
+    # varlen: at most 2^30 - 1 sequences
+    assert ws(args(B=1, T=1 << 20, N=(1 << 30), cu_seqlens=1 << 20))[0] == K.KDA_ERR_INVALID_ARG
+    st, n = ws(args(B=1, T=1 << 20, N=(1 << 20), cu_seqlens=1 << 20))
+    assert st == 0 and n > 0
+    # the backward's limits are the same
+    assert bwd_ws(bwd_args(B=1, T=64 * 2048, HV=hv, N=1))[0] == K.KDA_ERR_INVALID_ARG
+    assert bwd_ws(bwd_args(B=1, T=64 * 2047, HV=hv, N=1))[0] == 0
