@@ -74,6 +74,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m gated_delta_rule_chunked_amd.build`")
+    # torch ships its own HIP runtime; loaded first, it is the one libkda.so binds to, so
+    # that the library and torch's tensors and streams share one runtime (loaded the other
+    # way round, the process holds two runtimes and the library sees no device of torch's)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     P = ctypes.POINTER(KdaFwdArgs)
     lib.kda_fwd_workspace_bytes.argtypes = [P, ctypes.POINTER(c_size_t)]

@@ -148,3 +148,24 @@ def test_backward_and_forward_overlapping_on_separate_streams():
         for (a, outs, _ws), r in zip(calls, ref_b):
             assert all(torch.equal(o, q) for o, q in zip(outs, r))
         assert torch.equal(fkeep[0], ref_f[0]) and torch.equal(fkeep[1], ref_f[1])
+
+
+def test_library_loaded_before_torch_shares_its_runtime():
+    # a fresh process that loads the library before importing torch itself: the binding
+    # imports torch first, so both use one HIP runtime and a call on torch tensors works
+    import os
+    import subprocess
+    import sys
+    code = ("import gated_delta_rule_chunked_amd as pkg\n"
+            "pkg.load_library()\n"
+            "import torch\n"
+            "from synth.inputs import make_inputs\n"
+            "d = make_inputs(5, B=1, T=100, HQK=1, HV=2, K=64, V=32, has_h0=False)\n"
+            "t = {k: torch.from_numpy(d[k]).to(torch.bfloat16).cuda() for k in ('q', 'k', 'v', 'g', 'beta')}\n"
+            "o, ht = pkg.kda_fwd(t['q'], t['k'], t['v'], t['g'], t['beta'], scale=d['scale'])\n"
+            "torch.cuda.synchronize()\n"
+            "print('ok', bool(torch.isfinite(o.float()).all()))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "ok True" in r.stdout
