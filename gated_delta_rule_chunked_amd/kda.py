@@ -270,6 +270,14 @@ def kda_fwd(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, output_final
     if not q.is_cuda:
         raise RuntimeError("kda_fwd runs on the GPU only (tensors must be on a HIP device)")
     load_library()
+    with torch.cuda.device(q.device):   # the library launches on the current device
+        return _kda_fwd_on_device(q, k, v, g, beta, scale, h0, cu_seqlens, output_final_state, o, workspace,
+                                  beta_logits, state_dtype, output_chunk_states, seg_chunks, ht, hc, chunk)
+
+
+def _kda_fwd_on_device(q, k, v, g, beta, scale, h0, cu_seqlens, output_final_state, o, workspace, beta_logits,
+                       state_dtype, output_chunk_states, seg_chunks, ht, hc, chunk):
+    import torch
     B, T, _, K = q.shape
     HV, V = v.shape[2], v.shape[3]
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
@@ -380,6 +388,14 @@ def kda_bwd_dhu(qg, kg, w, g2, do, dv=None, dht=None, scale=None, cu_seqlens=Non
     if not qg.is_cuda:
         raise RuntimeError("kda_bwd_dhu runs on the GPU only (tensors must be on a HIP device)")
     load_library()
+    with torch.cuda.device(qg.device):   # the library launches on the current device
+        return _kda_bwd_dhu_on_device(qg, kg, w, g2, do, dv, dht, scale, cu_seqlens, state_dtype, checkpoint_dtype,
+                                      output_dh0, output_checkpoints, seg_chunks)
+
+
+def _kda_bwd_dhu_on_device(qg, kg, w, g2, do, dv, dht, scale, cu_seqlens, state_dtype, checkpoint_dtype,
+                           output_dh0, output_checkpoints, seg_chunks):
+    import torch
     B, T, HV, K = qg.shape
     V = do.shape[3]
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
