@@ -109,3 +109,14 @@ def test_bwd_many_sequences_library_plan(n_seq):
     got, ref = run_gpu(x, d), reference(x, d)
     check(got, ref, f"{n_seq} sequences")
     assert np.array_equal(got[2][7], gr["dht"][7].astype(np.float64))
+
+
+@pytest.mark.parametrize("seg", [0, 2])
+@pytest.mark.parametrize("K,V", [(128, 256), (64, 192), (128, 48)])
+def test_bwd_wide_and_narrow_values(seg, K, V):
+    # more value column groups than key column groups (V = 256 or 192: the state pass's
+    # groups past K / 64 carry b columns only), and a partial group (V = 48)
+    d = make_inputs(98, B=1, T=64 * 5 + 9, HQK=1, HV=2, K=K, V=V, has_h0=False)
+    gr = make_grads(d, 980)
+    x = scan_inputs(d, gr)
+    check(run_gpu(x, d, seg_chunks=seg), reference(x, d), f"K{K} V{V} seg {seg}")
