@@ -581,8 +581,17 @@ def main():
     kernels = []
     for k in keys:
         f = figs[k] or {}
-        kernels.append({"kernel": k, "necessary_bytes": necessary.get(_source_key(k), 0),
-                        "counter_bytes": f.get("bytes_per_launch"), "rocprof_avg_us": f.get("rocprof_avg_us")})
+        row = {"kernel": k, "necessary_bytes": necessary.get(_source_key(k), 0),
+               "counter_bytes": f.get("bytes_per_launch"), "rocprof_avg_us": f.get("rocprof_avg_us")}
+        if row["rocprof_avg_us"]:   # this kernel's own fraction: its necessary bytes over its average duration
+            row["achieved_GBs"] = row["necessary_bytes"] / (row["rocprof_avg_us"] * 1e-6) / 1e9
+            row["frac_of_hbm_peak"] = row["achieved_GBs"] / HBM_PEAK_GBS
+            if row["counter_bytes"]:
+                row["traffic_TBs"] = row["counter_bytes"] / (row["rocprof_avg_us"] * 1e-6) / 1e12
+        kernels.append(row)
+    timed = [r for r in kernels if r["rocprof_avg_us"]]
+    if timed:   # the kernel with the longest average duration
+        max(timed, key=lambda r: r["rocprof_avg_us"])["dominant"] = True
     calls = {}
     for name, arr, nb in (("intra", intra_ms, ab_intra), ("scan", inter_ms, ab_scan)):
         m = float(arr.mean())
